@@ -1,0 +1,166 @@
+/* mxmoe.h — C ABI of the MX-quantised sparse MoE expert block for AMD Instinct MI355X (gfx950).
+ *
+ * The block (per token t, bf16 activations x[t] of width H, bf16 router logits over E experts):
+ *   route   top-k experts by logit, softmax weights over the k selected, and the shared expert
+ *           (id E) appended as an always-selected slot with weight 1. The shared expert folded into
+ *           the routing table is the change described in "Lần theo điểm nghẽn: Tối ưu MiniMax M3 trên
+ *           AMD Instinct MI355X" (shared-expert passage, Fig. 4).
+ *   align   counting sort of the T*(k+1) slots into expert-contiguous, tile-padded blocks (the work
+ *           list of the grouped GEMMs; same page, local-shapes passage on grouped MoE programs).
+ *   quant   x -> MXFP8 (E4M3 codes, one E8M0 scale per 32 along H), once per token.
+ *   gate_up grouped GEMM over the routed + shared experts on gfx950 block-scaled MFMA, SwiGLU
+ *           (SiLU(gate) * up) epilogue, requantised to MXFP8 along I.
+ *   down    grouped GEMM, then the top-k weighted combine back to token order ("finalize", fused
+ *           into the GEMM epilogue as in "Tối ưu hiệu năng Kimi K3 trong vLLM", deferred-finalize
+ *           passage), and one rounding to bf16.
+ * Weights are MXFP8 (E4M3) or MXFP4 (E2M1) with 32-element blocks and E8M0 scales along K, or
+ * plain bf16. Encodings follow the OCP Microscaling Formats (MX) v1.0 specification.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory owned by the caller unless a comment says "host". The library
+ *     never allocates, frees, aborts, throws or exits.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued on it
+ *     and the call returns without synchronising; nothing crosses back to the host (counts stay on
+ *     the GPU, as the batch-1 decode page "Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên
+ *     4 GPU Blackwell" requires in "Hình dạng của một bước batch-1"), so calls are capturable.
+ *   - Arguments are validated on the host before any HIP call; a failure returns a negative status
+ *     and enqueues nothing. A launch failure returns MXMOE_EHIP. Faults inside a kernel surface at
+ *     the caller's next synchronisation. T = 0 is a no-op returning MXMOE_OK.
+ *   - Inputs must be finite (NaN/Inf logits or activations are a precondition violation).
+ *   - Concurrent calls need distinct outputs and workspaces.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------------------------- status */
+enum {
+  MXMOE_OK = 0,
+  MXMOE_EINVAL = -1,       /* null pointer, bad size, bad shape */
+  MXMOE_EUNSUPPORTED = -2, /* valid but not implemented (format pair, shape class) */
+  MXMOE_EWORKSPACE = -3,   /* workspace too small or misaligned */
+  MXMOE_EHIP = -4          /* a HIP launch failed */
+};
+
+/* Data formats. */
+enum {
+  MXMOE_BF16 = 0,
+  MXMOE_F32 = 1,
+  MXMOE_MXFP8_E4M3 = 2, /* one code per byte */
+  MXMOE_MXFP4_E2M1 = 3  /* two codes per byte: element 2i in the low nibble, 2i+1 in the high */
+};
+
+/* Launcher choice (small-M = expert-major decode grid, large-M = block-major prefill grid). */
+enum { MXMOE_LAUNCH_AUTO = 0, MXMOE_LAUNCH_SMALL_M = 1, MXMOE_LAUNCH_LARGE_M = 2 };
+/* Combine of the k+1 slot outputs of a token: per-slot rows summed in a fixed order
+   (deterministic) or fp32 atomics into a token-major accumulator (order varies run to run). */
+enum { MXMOE_COMBINE_AUTO = 0, MXMOE_COMBINE_SLOTS = 1, MXMOE_COMBINE_ATOMIC = 2 };
+
+/* Problem shape. Requirements: T >= 0; H % 128 == 0; I % 32 == 0; 1 <= top_k <= E <= 1024;
+   w_fmt in {BF16, MXFP8_E4M3, MXFP4_E2M1}; act_fmt = MXFP8_E4M3 for MX weights and BF16 for bf16
+   weights; logits_dtype in {BF16, F32}. */
+typedef struct {
+  int32_t T, H, E, top_k, I;
+  int32_t w_fmt, act_fmt, logits_dtype;
+} mxmoe_shape;
+
+/* Optional knobs for A/B runs and tests; all-zero = automatic. */
+typedef struct {
+  int32_t launcher; /* MXMOE_LAUNCH_* */
+  int32_t combine;  /* MXMOE_COMBINE_* */
+  int32_t block_m;  /* align tile height (16, 32, 64, 128, 256); 0 = the launcher's default */
+  int32_t reserved;
+} mxmoe_options;
+
+/* Host: static description of a status code. Never NULL. */
+const char* mxmoe_status_string(int status);
+
+/* --------------------------------------------------------------------------------- route
+ * Top-k routing with the fixed lowest-index tie-break.
+ * logits   [T, E] row-major, bf16 or fp32 (logits_dtype).
+ * topk_ids [T, top_k+1] int32: for each token the top_k experts ordered by (logit descending,
+ *          expert index ascending), -0 equal to +0; slot top_k holds the shared expert id E.
+ * topk_w   [T, top_k+1] fp32: exp(l_j - l_0) / sum_{i<top_k} exp(l_i - l_0) for j < top_k
+ *          (softmax renormalised over the selected experts); slot top_k holds exactly 1.0.
+ * Selection compares logits, not probabilities (softmax is monotone; the MiniMax-M3 page's
+ * speculative-indexer passage: a positive rescale cannot change a top-k order). */
+int mxmoe_route(const void* logits, int T, int E, int top_k, int logits_dtype,
+                int32_t* topk_ids, float* topk_w, void* stream);
+
+/* --------------------------------------------------------------------------------- align
+ * Counting sort of the flat slots f = t*(top_k+1) + j (S = T*(top_k+1) of them) by expert.
+ * Experts 0..E (shared last) in ascending id order; within an expert ascending f (stable); each
+ * expert's run is padded with the sentinel S to a multiple of block_m; experts with no slot get no
+ * block. Outputs (sizes from mxmoe_align_capacity, cap = elements of sorted_ids):
+ *   sorted_ids   [cap]          slot ids, S in padding and past the end
+ *   block_expert [cap/block_m]  expert of each tile, -1 past the last used tile
+ *   num_post_pad [1]            padded slot count in use
+ *   expert_off   [E+2]          start of each expert's run (expert_off[E+1] = num_post_pad); may
+ *                               be NULL
+ * workspace: mxmoe_align_workspace_bytes(...) bytes of device scratch (may be 0 / NULL when that
+ * returns 0). block_m in {16, 32, 64, 128, 256}. */
+size_t mxmoe_align_capacity(int T, int E, int top_k, int block_m);       /* host; 0 if invalid */
+size_t mxmoe_align_workspace_bytes(int T, int E, int top_k, int block_m); /* host */
+int mxmoe_align(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------ quantize
+ * MX quantisation of a row-major matrix src [rows, K] (bf16 or fp32, finite) along K, one scale
+ * per 32 elements: shared_exp = floor(log2(max|x|)) - emax (8 for E4M3, 2 for E2M1) clamped to
+ * [-127, 127]; scale byte = shared_exp + 127 (0 for an all-zero block); each element rounded to
+ * the nearest code of x / 2^shared_exp, ties to even, saturating (448 / 6), sign kept.
+ * codes  [rows, K] (MXFP8) or [rows, K/2] (MXFP4, low nibble first); scales [rows, K/32].
+ * K % 32 == 0. The same rule quantises activations inside mxmoe_forward; this entry point is for
+ * weights at load time. */
+int mxmoe_quantize(const void* src, int rows, int K, int src_dtype, int fmt, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------------- prepack
+ * Converts canonical expert weights into the kernel-native, fragment-major layout, once at load
+ * (the MiniMax-M3 page, shared-expert passage: weight and scale reordering moved to model load;
+ * the serving loop uses the prepared form directly).
+ * Canonical layouts (row-major, K contiguous; expert E is the shared expert):
+ *   w13 [E+1, 2I, H] codes (gate rows 0..I-1, then up rows I..2I-1), s13 [E+1, 2I, H/32]
+ *   w2  [E+1, H, I]  codes,                                            s2  [E+1, H, I/32]
+ * Codes are bf16 values for BF16 weights (s13/s2 then NULL), one byte per code for MXFP8, two per
+ * byte (low nibble first) for MXFP4. Output buffer sizes: mxmoe_prepacked_bytes(s, which) with
+ * which = 0 (w13_p), 1 (s13_p), 2 (w2_p), 3 (s2_p); 0 for the scale buffers of BF16 weights. */
+size_t mxmoe_prepacked_bytes(const mxmoe_shape* s, int which);
+int mxmoe_prepack(const mxmoe_shape* s, const void* w13, const uint8_t* s13, const void* w2,
+                  const uint8_t* s2, void* w13_p, void* s13_p, void* w2_p, void* s2_p,
+                  void* stream);
+
+/* ------------------------------------------------------------------------------- forward
+ * The whole block. x [T, H] bf16; logits [T, E] (logits_dtype); prepacked weights from
+ * mxmoe_prepack; y [T, H] bf16, overwritten. workspace: device scratch of at least
+ * mxmoe_workspace_bytes(s) (or _ex with the same options), 256-byte aligned; its contents need
+ * no initialisation and are clobbered. */
+size_t mxmoe_workspace_bytes(const mxmoe_shape* s);
+size_t mxmoe_workspace_bytes_ex(const mxmoe_shape* s, const mxmoe_options* opt);
+int mxmoe_forward(const mxmoe_shape* s, const void* x, const void* logits, const void* w13_p,
+                  const void* s13_p, const void* w2_p, const void* s2_p, void* y,
+                  void* workspace, size_t workspace_bytes, void* stream);
+int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void* x,
+                     const void* logits, const void* w13_p, const void* s13_p, const void* w2_p,
+                     const void* s2_p, void* y, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Host: where forward keeps an intermediate inside its workspace, for inspection after the call
+ * (routing table, sorted layout, quantised activations). which: 0 topk_ids, 1 topk_w,
+ * 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off. Returns the byte offset and writes
+ * the byte size to *bytes; the tile height forward used is written to *block_m. Returns
+ * (size_t)-1 for an invalid request. */
+size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int which,
+                            size_t* bytes, int* block_m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXMOE_H */

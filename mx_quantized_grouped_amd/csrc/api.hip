@@ -1,0 +1,346 @@
+// C ABI of the MX MoE block: argument validation, workspace plan, launcher choice and the launch
+// sequence route -> align -> quant -> gate_up (+SwiGLU, requant) -> down (+weighted combine) ->
+// bf16 output. Everything is enqueued on the caller's stream; nothing is read back to the host.
+#include <cstdio>
+#include <cstdlib>
+
+#include "mxmoe.h"
+#include "device.h"
+#include "kernels.h"
+
+using namespace mxmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int wf_of(int w_fmt) {
+  return w_fmt == MXMOE_MXFP8_E4M3 ? WF_FP8 : (w_fmt == MXMOE_MXFP4_E2M1 ? WF_FP4 : WF_BF16);
+}
+
+// Row size in bytes of the kernel-native scale layout for a K-long row.
+int scale_row_bytes(int K) {
+  int nks = (K + KSTEP - 1) / KSTEP;
+  return 16 * ((nks + 3) / 4);
+}
+
+size_t cap_of(int S, int E1, int bm) {
+  size_t cap = (size_t)S + (size_t)(E1 < S ? E1 : S) * (bm - 1);
+  return (cap + bm - 1) / bm * bm;
+}
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+int check_route_args(int T, int E, int top_k) {
+  if (T < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > E) return MXMOE_EINVAL;
+  if (top_k > kMaxTopK) return MXMOE_EUNSUPPORTED;
+  if ((long long)T * (top_k + 1) > (1LL << 30)) return MXMOE_EUNSUPPORTED;
+  return MXMOE_OK;
+}
+
+int check_shape(const mxmoe_shape* s) {
+  if (!s) return MXMOE_EINVAL;
+  int rc = check_route_args(s->T, s->E, s->top_k);
+  if (rc) return rc;
+  if (s->H <= 0 || s->I <= 0 || s->H % 32 || s->I % 32) return MXMOE_EINVAL;
+  if (s->H % 128) return MXMOE_EUNSUPPORTED;
+  if (s->logits_dtype != MXMOE_BF16 && s->logits_dtype != MXMOE_F32) return MXMOE_EINVAL;
+  bool mxw = s->w_fmt == MXMOE_MXFP8_E4M3 || s->w_fmt == MXMOE_MXFP4_E2M1;
+  if (!mxw && s->w_fmt != MXMOE_BF16) return MXMOE_EINVAL;
+  if (mxw && s->act_fmt != MXMOE_MXFP8_E4M3) return MXMOE_EUNSUPPORTED;
+  if (!mxw && s->act_fmt != MXMOE_BF16) return MXMOE_EUNSUPPORTED;
+  return MXMOE_OK;
+}
+
+enum Seg {
+  SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF, SEG_TOUCHED, SEG_ALIGN,
+  SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, NSEG
+};
+
+struct Plan {
+  int T, H, E, k, I, k1, S, E1;
+  int wf;
+  bool mx, large;
+  int combine;  // 1 slots, 2 atomic
+  int bm, cap, Ip, srs_H, srs_I;
+  size_t off[NSEG + 1];
+};
+
+int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0};
+  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 2) return MXMOE_EINVAL;
+  if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
+  Plan& p = *P;
+  p.T = s->T; p.H = s->H; p.E = s->E; p.k = s->top_k; p.I = s->I;
+  p.k1 = p.k + 1; p.S = p.T * p.k1; p.E1 = p.E + 1;
+  p.wf = wf_of(s->w_fmt);
+  p.mx = p.wf != WF_BF16;
+  // Launcher: block-major (large-M) once the average expert holds enough rows to fill tiles.
+  p.large = o.launcher == MXMOE_LAUNCH_LARGE_M ||
+            (o.launcher == MXMOE_LAUNCH_AUTO && p.S >= 16 * p.E1);
+  p.combine = o.combine ? o.combine : (p.large ? MXMOE_COMBINE_ATOMIC : MXMOE_COMBINE_SLOTS);
+  p.bm = o.block_m ? o.block_m : (p.large ? 64 : 16);
+  p.cap = (int)cap_of(p.S, p.E1, p.bm);
+  p.Ip = round_up(p.I, KSTEP);
+  p.srs_H = scale_row_bytes(p.H);
+  p.srs_I = scale_row_bytes(p.Ip);
+  size_t sz[NSEG];
+  sz[SEG_IDS] = (size_t)p.S * 4;
+  sz[SEG_W] = (size_t)p.S * 4;
+  sz[SEG_SORTED] = (size_t)p.cap * 4;
+  sz[SEG_BLOCKEXP] = (size_t)(p.cap / p.bm) * 4;
+  sz[SEG_COUNTERS] = 16;
+  sz[SEG_EXPOFF] = (size_t)(p.E1 + 1) * 4;
+  sz[SEG_TOUCHED] = (size_t)p.E1 * 4;
+  sz[SEG_ALIGN] = align_scratch_bytes(p.T, p.E, p.k);
+  sz[SEG_XQ] = p.mx ? (size_t)p.T * p.H : 0;
+  sz[SEG_XS] = p.mx ? (size_t)p.T * p.srs_H : 0;
+  sz[SEG_H] = (size_t)p.cap * p.Ip * (p.mx ? 1 : 2);
+  sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
+  sz[SEG_OUT] = (size_t)(p.combine == MXMOE_COMBINE_SLOTS ? p.S : p.T) * p.H * 4;
+  size_t at = 0;
+  for (int i = 0; i < NSEG; ++i) {
+    p.off[i] = at;
+    at += up(sz[i]);
+  }
+  p.off[NSEG] = at;
+  return MXMOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MXMOE_OK : MXMOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxmoe_status_string(int status) {
+  switch (status) {
+    case MXMOE_OK: return "ok";
+    case MXMOE_EINVAL: return "invalid argument";
+    case MXMOE_EUNSUPPORTED: return "unsupported shape or format";
+    case MXMOE_EWORKSPACE: return "workspace too small or misaligned";
+    case MXMOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mxmoe_route(const void* logits, int T, int E, int top_k, int logits_dtype, int32_t* topk_ids,
+                float* topk_w, void* stream) {
+  int rc = check_route_args(T, E, top_k);
+  if (rc) return rc;
+  if (logits_dtype != MXMOE_BF16 && logits_dtype != MXMOE_F32) return MXMOE_EINVAL;
+  if (T == 0) return MXMOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MXMOE_EINVAL;
+  if (!aligned(logits, logits_dtype == MXMOE_F32 ? 4 : 2) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return MXMOE_EINVAL;
+  return hip_status(launch_route(logits, logits_dtype == MXMOE_F32, T, E, top_k, topk_ids, topk_w,
+                                 (hipStream_t)stream));
+}
+
+size_t mxmoe_align_capacity(int T, int E, int top_k, int block_m) {
+  if (check_route_args(T, E, top_k) || !valid_block_m(block_m)) return 0;
+  return cap_of(T * (top_k + 1), E + 1, block_m);
+}
+
+size_t mxmoe_align_workspace_bytes(int T, int E, int top_k, int block_m) {
+  if (check_route_args(T, E, top_k) || !valid_block_m(block_m)) return 0;
+  return align_scratch_bytes(T, E, top_k);
+}
+
+int mxmoe_align(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_route_args(T, E, top_k);
+  if (rc) return rc;
+  if (!valid_block_m(block_m)) return MXMOE_EINVAL;
+  if (T == 0) return MXMOE_OK;
+  if (!topk_ids || !sorted_ids || !block_expert || !num_post_pad) return MXMOE_EINVAL;
+  size_t need = align_scratch_bytes(T, E, top_k);
+  if (need && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
+    return MXMOE_EWORKSPACE;
+  return hip_status(launch_align(topk_ids, T, E, top_k, block_m, sorted_ids, block_expert,
+                                 num_post_pad, expert_off, nullptr, nullptr, workspace,
+                                 (hipStream_t)stream));
+}
+
+int mxmoe_quantize(const void* src, int rows, int K, int src_dtype, int fmt, uint8_t* codes,
+                   uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32) return MXMOE_EINVAL;
+  if (src_dtype != MXMOE_BF16 && src_dtype != MXMOE_F32) return MXMOE_EINVAL;
+  if (fmt != MXMOE_MXFP8_E4M3 && fmt != MXMOE_MXFP4_E2M1) return MXMOE_EINVAL;
+  if (rows == 0) return MXMOE_OK;
+  if (!src || !codes || !scales) return MXMOE_EINVAL;
+  if (!aligned(src, 16) || !aligned(codes, 16)) return MXMOE_EINVAL;
+  return hip_status(launch_quantize_canonical(src, src_dtype == MXMOE_F32, rows, K,
+                                              fmt == MXMOE_MXFP4_E2M1, codes, scales,
+                                              (hipStream_t)stream));
+}
+
+static PrepackDims dims_of(const mxmoe_shape* s, bool w13) {
+  PrepackDims d;
+  d.E1 = s->E + 1;
+  d.N = w13 ? 2 * s->I : s->H;
+  d.K = w13 ? s->H : s->I;
+  d.wf = wf_of(s->w_fmt);
+  d.w13 = w13;
+  d.I = s->I;
+  return d;
+}
+
+size_t mxmoe_prepacked_bytes(const mxmoe_shape* s, int which) {
+  if (check_shape(s) || which < 0 || which > 3) return 0;
+  PrepackDims d = dims_of(s, which < 2);
+  return (which & 1) ? prepack_scale_bytes(d) : prepack_code_bytes(d);
+}
+
+int mxmoe_prepack(const mxmoe_shape* s, const void* w13, const uint8_t* s13, const void* w2,
+                  const uint8_t* s2, void* w13_p, void* s13_p, void* w2_p, void* s2_p,
+                  void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  bool mx = s->w_fmt != MXMOE_BF16;
+  if (!w13 || !w2 || !w13_p || !w2_p) return MXMOE_EINVAL;
+  if (mx && (!s13 || !s2 || !s13_p || !s2_p)) return MXMOE_EINVAL;
+  if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_p, 16) || !aligned(w2_p, 16))
+    return MXMOE_EINVAL;
+  if (mx && (!aligned(s13_p, 4) || !aligned(s2_p, 4))) return MXMOE_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_prepack(dims_of(s, true), w13, s13, w13_p, s13_p, st);
+  if (e == hipSuccess) e = launch_prepack(dims_of(s, false), w2, s2, w2_p, s2_p, st);
+  return hip_status(e);
+}
+
+size_t mxmoe_workspace_bytes_ex(const mxmoe_shape* s, const mxmoe_options* opt) {
+  Plan p;
+  if (make_plan(s, opt, &p)) return 0;
+  return p.off[NSEG];
+}
+
+size_t mxmoe_workspace_bytes(const mxmoe_shape* s) { return mxmoe_workspace_bytes_ex(s, nullptr); }
+
+size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int which,
+                            size_t* bytes, int* block_m) {
+  Plan p;
+  if (make_plan(s, opt, &p)) return (size_t)-1;
+  static const int segs[6] = {SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF};
+  if (which < 0 || which > 5) return (size_t)-1;
+  size_t sz[6] = {(size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4,
+                  (size_t)(p.cap / p.bm) * 4, 4, (size_t)(p.E1 + 1) * 4};
+  if (bytes) *bytes = sz[which];
+  if (block_m) *block_m = p.bm;
+  return p.off[segs[which]];
+}
+
+int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void* x,
+                     const void* logits, const void* w13_p, const void* s13_p, const void* w2_p,
+                     const void* s2_p, void* y, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  Plan P;
+  int rc = make_plan(s, opt, &P);
+  if (rc) return rc;
+  if (P.T == 0) return MXMOE_OK;
+  if (!x || !logits || !w13_p || !w2_p || !y) return MXMOE_EINVAL;
+  if (P.mx && (!s13_p || !s2_p)) return MXMOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w13_p, 16) || !aligned(w2_p, 16) ||
+      !aligned(logits, s->logits_dtype == MXMOE_F32 ? 4 : 2))
+    return MXMOE_EINVAL;
+  if (!workspace || workspace_bytes < P.off[NSEG] || !aligned(workspace, kAlign))
+    return MXMOE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* ids = (int32_t*)(ws + P.off[SEG_IDS]);
+  float* tw = (float*)(ws + P.off[SEG_W]);
+  int32_t* sorted = (int32_t*)(ws + P.off[SEG_SORTED]);
+  int32_t* bexp = (int32_t*)(ws + P.off[SEG_BLOCKEXP]);
+  int32_t* counters = (int32_t*)(ws + P.off[SEG_COUNTERS]);  // [0] num_post_pad, [1] n_touched
+  int32_t* eoff = (int32_t*)(ws + P.off[SEG_EXPOFF]);
+  int32_t* touched = (int32_t*)(ws + P.off[SEG_TOUCHED]);
+  void* aws = ws + P.off[SEG_ALIGN];
+  uint8_t* xq = (uint8_t*)(ws + P.off[SEG_XQ]);
+  uint8_t* xs = (uint8_t*)(ws + P.off[SEG_XS]);
+  uint8_t* h = (uint8_t*)(ws + P.off[SEG_H]);
+  uint8_t* hs = (uint8_t*)(ws + P.off[SEG_HS]);
+  float* out32 = (float*)(ws + P.off[SEG_OUT]);
+  const bool slots = P.combine == MXMOE_COMBINE_SLOTS;
+
+  if (getenv("MXMOE_TRACE"))
+    fprintf(stderr, "mxmoe_forward: T=%d H=%d E=%d k=%d I=%d w=%d launcher=%s block_m=%d combine=%s\n",
+            P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.large ? "large_m" : "small_m", P.bm,
+            slots ? "slots" : "atomic");
+
+  hipError_t e = launch_route(logits, s->logits_dtype == MXMOE_F32, P.T, P.E, P.k, ids, tw, st);
+  if (e == hipSuccess)
+    e = launch_align(ids, P.T, P.E, P.k, P.bm, sorted, bexp, counters, eoff, touched,
+                     counters + 1, aws, st);
+  if (e == hipSuccess) {
+    if (P.mx)
+      e = launch_quantize_act((const uint16_t*)x, P.T, P.H, xq, xs, P.srs_H,
+                              slots ? nullptr : out32, st);
+    else if (!slots)
+      e = launch_zero_f32(out32, (size_t)P.T * P.H, st);
+  }
+  const int grid_y = P.large ? P.cap / P.bm : (P.E1 < P.S ? P.E1 : P.S);
+  GemmParams g{};
+  g.sorted_ids = sorted;
+  g.expert_off = eoff;
+  g.touched = touched;
+  g.n_touched = counters + 1;
+  g.block_expert = bexp;
+  g.num_post_pad = counters;
+  g.block_m = P.bm;
+  g.S = P.S;
+  g.k1 = P.k1;
+  g.I = P.I;
+  g.Ip = P.Ip;
+  g.H = P.H;
+  g.h = h;
+  g.hs = hs;
+  g.h_stride = P.Ip * (P.mx ? 1 : 2);
+  g.h_srs = P.srs_I;
+  g.topk_w = tw;
+  g.out32 = out32;
+  g.combine = P.combine;
+  if (e == hipSuccess) {
+    GemmParams gu = g;
+    gu.a = P.mx ? xq : (const uint8_t*)x;
+    gu.as = xs;
+    gu.a_stride = P.mx ? P.H : 2 * P.H;
+    gu.a_srs = P.srs_H;
+    gu.w = (const uint8_t*)w13_p;
+    gu.ws = (const uint8_t*)s13_p;
+    gu.NT = 2 * P.I / 16;
+    gu.NKS = P.H / KSTEP;
+    gu.NKG = (gu.NKS + 3) / 4;
+    e = launch_gate_up(P.wf, P.large, gu, grid_y, st);
+  }
+  if (e == hipSuccess) {
+    GemmParams dn = g;
+    dn.a = h;
+    dn.as = hs;
+    dn.a_stride = g.h_stride;
+    dn.a_srs = P.srs_I;
+    dn.w = (const uint8_t*)w2_p;
+    dn.ws = (const uint8_t*)s2_p;
+    dn.NT = P.H / 16;
+    dn.NKS = P.Ip / KSTEP;
+    dn.NKG = (dn.NKS + 3) / 4;
+    e = launch_down(P.wf, P.large, dn, grid_y, st);
+  }
+  if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, slots, (uint16_t*)y, st);
+  return hip_status(e);
+}
+
+int mxmoe_forward(const mxmoe_shape* s, const void* x, const void* logits, const void* w13_p,
+                  const void* s13_p, const void* w2_p, const void* s2_p, void* y,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  return mxmoe_forward_ex(s, nullptr, x, logits, w13_p, s13_p, w2_p, s2_p, y, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Device helpers shared by the MX MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// K elements consumed by one block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
+constexpr int KSTEP = 128;
+// Weight formats of the B operand.
+enum WFmt { WF_FP8 = 0, WF_FP4 = 1, WF_BF16 = 2 };
+
+// ---------------------------------------------------------------------------- lane helpers
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
+}
+
+// ---------------------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------------------- MX encoding
+// floor(log2(a)) for finite a > 0 (fp32 subnormals included), from the exponent bits.
+__device__ __forceinline__ int floor_log2(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF);
+  if (e == 0) return 31 - __clz(u & 0x7FFFFF) - 149;
+  return e - 127;
+}
+
+// Shared exponent of an MX block: floor(log2(amax)) - emax_elem, clamped to [-127, 127];
+// an all-zero block gets -127 (scale byte 0).
+template <int EMAX>
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int se = floor_log2(amax) - EMAX;
+  return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// E4M3 magnitude code of a in [0, 448]: round to nearest, ties to even.
+__device__ __forceinline__ uint32_t e4m3_mag(float a) {
+  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal grid m * 2^-9
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);                                  // keep 3 mantissa bits
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);               // rebias 127 -> 7
+}
+// E2M1 magnitude code of a in [0, 6].
+__device__ __forceinline__ uint32_t e2m1_mag(float a) {
+  if (a < 1.0f) return (uint32_t)__builtin_rintf(a * 2.0f);          // 0, 0.5, 1.0 (code 2)
+  uint32_t u = __float_as_uint(a);
+  u += 0x1FFFFFu + ((u >> 22) & 1u);                                 // keep 1 mantissa bit
+  return (((u >> 23) - 126u) << 1) | ((u >> 22) & 1u);               // rebias 127 -> 1
+}
+// Element code of x in a block with shared exponent se (sign kept, saturating).
+__device__ __forceinline__ uint32_t e4m3_code(float x, int se) {
+  float v = ldexpf(x, -se);
+  uint32_t m = e4m3_mag(fminf(fabsf(v), 448.0f));
+  return m | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+__device__ __forceinline__ uint32_t e2m1_code(float x, int se) {
+  float v = ldexpf(x, -se);
+  uint32_t m = e2m1_mag(fminf(fabsf(v), 6.0f));
+  return m | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// ---------------------------------------------------------------------------- layouts
+// Kernel-native scale layout of an activation / intermediate row: the scale of K-block kb lives
+// at byte 16*(ks/4) + 4*(kb%4) + ks%4, ks = kb/4 the MFMA K-step. One dword load at
+// 16*kg + 4*g then gives lane group g the scales of four consecutive K-steps (byte ks%4).
+__device__ __host__ __forceinline__ int act_scale_byte(int kb) {
+  int ks = kb >> 2;
+  return ((ks >> 2) << 4) + ((kb & 3) << 2) + (ks & 3);
+}
+__device__ __host__ __forceinline__ int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+}  // namespace mxmoe

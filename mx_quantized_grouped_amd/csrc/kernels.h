@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels. Host code only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+constexpr int kMaxTopK = 63;      // one wave holds the selected experts, lane top_k the shared slot
+constexpr int kMaxExperts = 1024; // routed experts; E + 1 <= 2048 for the block-wide scans
+constexpr int kAlignSmallMaxSlots = 4096;
+constexpr int kAlignChunk = 1024; // slots per workgroup in the multi-workgroup sort
+
+// route.hip
+hipError_t launch_route(const void* logits, bool logits_f32, int T, int E, int top_k,
+                        int32_t* ids, float* w, hipStream_t st);
+
+// align.hip
+size_t align_scratch_bytes(int T, int E, int top_k);
+hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                        int32_t* expert_off, int32_t* touched, int32_t* n_touched, void* scratch,
+                        hipStream_t st);
+
+// quant.hip
+// Canonical MX quantisation (codes row-major, scales [rows, K/32]).
+hipError_t launch_quantize_canonical(const void* src, bool src_f32, int rows, int K, bool fp4,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t st);
+// Activation rows -> MXFP8 in the kernel-native layout (codes [T, H], scales [T, srs]); when
+// zero_out != nullptr also clears zero_out[T, H] (fp32), the atomic-combine accumulator.
+hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs,
+                               int srs, float* zero_out, hipStream_t st);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
+
+// prepack.hip
+struct PrepackDims {
+  int E1;      // experts incl. shared
+  int N;       // rows per expert (2I for w13, H for w2)
+  int K;       // reduction length (H for w13, I for w2)
+  int wf;      // WF_FP8 / WF_FP4 / WF_BF16
+  bool w13;    // interleave gate/up 16-row tiles
+  int I;       // for the w13 interleave
+};
+size_t prepack_code_bytes(const PrepackDims& d);
+size_t prepack_scale_bytes(const PrepackDims& d);
+hipError_t launch_prepack(const PrepackDims& d, const void* codes, const uint8_t* scales,
+                          void* codes_p, void* scales_p, hipStream_t st);
+
+// gemm.hip
+struct GemmParams {
+  const uint8_t* a;          // A rows: MX codes or bf16
+  const uint8_t* as;         // A kernel-native scales (MX)
+  int a_stride;              // bytes per A row
+  int a_srs;                 // bytes per A scale row
+  const uint8_t* w;          // prepacked weights
+  const uint8_t* ws;         // prepacked weight scales (MX)
+  int NT, NKS, NKG;          // per expert: 16-row N tiles, K-steps of 128, groups of 4 K-steps
+  const int32_t* sorted_ids;
+  const int32_t* expert_off;
+  const int32_t* touched;
+  const int32_t* n_touched;
+  const int32_t* block_expert;
+  const int32_t* num_post_pad;
+  int block_m, S, k1;
+  // gate_up epilogue
+  uint8_t* h;                // intermediate rows [cap, Ip] (MXFP8 codes or bf16)
+  uint8_t* hs;               // intermediate scales [cap, h_srs]
+  int h_stride, h_srs, I, Ip;
+  // down epilogue
+  const float* topk_w;
+  float* out32;              // slot rows [S, H] or token rows [T, H]
+  int H;
+  int combine;               // 1 slots, 2 atomic
+};
+hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
+hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
+
+// finalize.hip
+hipError_t launch_finalize(const float* out32, int T, int H, int k1, bool slots, uint16_t* y,
+                           hipStream_t st);
+
+}  // namespace mxmoe

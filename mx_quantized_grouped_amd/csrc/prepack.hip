@@ -1,0 +1,133 @@
+// Load-time conversion of canonical expert weights into the kernel-native, fragment-major layout
+// (the reordering of MXFP8 weights and scales moved to model load in "Lần theo điểm nghẽn: Tối ưu
+// MiniMax M3 trên AMD Instinct MI355X", shared-expert/AITER passage).
+//
+// A fragment is one 16-row x 128-K tile of an expert's weight matrix, stored exactly in the order a
+// wavefront's lanes consume it as the B operand of one gfx950 MFMA, so each wave load of a fragment
+// is a contiguous 1 KiB:
+//   MXFP8 (2 KiB): [half h][lane l][16 B]; lane l = n + 16 g holds row n, K = 16g..16g+15 (h = 0)
+//                  and 64+16g..64+16g+15 (h = 1) of the tile — the operand order of
+//                  v_mfma_scale_f32_16x16x128_f8f6f4 for 8-bit elements.
+//   MXFP4 (1 KiB): [lane l][16 B]; lane l holds row n, K = 32g..32g+31, low nibble first.
+//   bf16  (4 KiB): [sub-step s][lane l][16 B]; lane l holds row n, K = 32s+8g..32s+8g+7 (the
+//                  v_mfma_f32_16x16x32_bf16 operand order, four per 128-K step).
+// Fragments of an expert are ordered [16-row tile nt][K-step ks]. For W13 the tiles alternate gate
+// and up: tile 2p holds gate rows 16p..16p+15 and tile 2p+1 up rows I+16p..I+16p+15, so one wave
+// holds matching gate and up columns for the SwiGLU epilogue.
+// Scales: per (expert, tile nt, group of four K-steps kg) 64 dwords; lane l = n + 16g holds in byte j
+// the scale of row n, K-block 4*(4kg + j) + g (the operand order of the MFMA scale register, byte j
+// selected for K-step 4kg + j). K is zero-padded to a multiple of 128 (scale byte 127 there).
+#include "device.h"
+#include "kernels.h"
+
+namespace mxmoe {
+
+namespace {
+
+__device__ __forceinline__ int src_row(int nt, int n, bool w13, int I) {
+  if (!w13) return nt * 16 + n;
+  int p = nt >> 1;
+  return (nt & 1) ? I + p * 16 + n : p * 16 + n;
+}
+
+// One thread per 16-byte chunk of the prepacked codes.
+template <int WF>
+__global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t* src, uint8_t* dst, int E1,
+                                                       int N, int K, bool w13, int I) {
+  constexpr int FB = WF == WF_FP8 ? 2048 : (WF == WF_FP4 ? 1024 : 4096);
+  constexpr int CH = FB / 16;  // chunks per fragment
+  const int NT = N / 16, NKS = (K + KSTEP - 1) / KSTEP;
+  size_t chunk = (size_t)blockIdx.x * 256 + threadIdx.x;
+  size_t total = (size_t)E1 * NT * NKS * CH;
+  if (chunk >= total) return;
+  int c = (int)(chunk % CH);
+  size_t frag = chunk / CH;
+  int ks = (int)(frag % NKS);
+  size_t en = frag / NKS;
+  int nt = (int)(en % NT);
+  size_t e = en / NT;
+  int l, kin;  // lane, first K index (within the step) of this chunk
+  if (WF == WF_FP8) {
+    int h = c >> 6;
+    l = c & 63;
+    kin = 64 * h + 16 * (l >> 4);
+  } else if (WF == WF_FP4) {
+    l = c;
+    kin = 32 * (l >> 4);
+  } else {
+    int s = c >> 6;
+    l = c & 63;
+    kin = 32 * s + 8 * (l >> 4);
+  }
+  int row = src_row(nt, l & 15, w13, I);
+  int k = ks * KSTEP + kin;
+  v4i val = v4i{0, 0, 0, 0};
+  if (k < K) {
+    size_t rb = (size_t)e * N + row;
+    if (WF == WF_FP8) val = *(const v4i*)(src + rb * K + k);
+    else if (WF == WF_FP4) val = *(const v4i*)(src + rb * (K / 2) + k / 2);
+    else val = *(const v4i*)(src + (rb * K + k) * 2);
+  }
+  *(v4i*)(dst + chunk * 16) = val;
+}
+
+// One thread per prepacked scale dword.
+__global__ __launch_bounds__(256) void k_prepack_scales(const uint8_t* src, uint32_t* dst, int E1,
+                                                        int N, int K, bool w13, int I) {
+  const int NT = N / 16, NKS = (K + KSTEP - 1) / KSTEP, NKG = (NKS + 3) / 4, KB = K / 32;
+  size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  size_t total = (size_t)E1 * NT * NKG * 64;
+  if (idx >= total) return;
+  int l = (int)(idx & 63);
+  size_t r = idx >> 6;
+  int kg = (int)(r % NKG);
+  size_t en = r / NKG;
+  int nt = (int)(en % NT);
+  size_t e = en / NT;
+  int row = src_row(nt, l & 15, w13, I), g = l >> 4;
+  const uint8_t* s = src + ((size_t)e * N + row) * KB;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int kb = 4 * (4 * kg + j) + g;
+    uint32_t b = kb < KB ? s[kb] : 127u;
+    v |= b << (8 * j);
+  }
+  dst[idx] = v;
+}
+
+}  // namespace
+
+size_t prepack_code_bytes(const PrepackDims& d) {
+  size_t FB = d.wf == WF_FP8 ? 2048 : (d.wf == WF_FP4 ? 1024 : 4096);
+  size_t NKS = (d.K + KSTEP - 1) / KSTEP;
+  return (size_t)d.E1 * (d.N / 16) * NKS * FB;
+}
+
+size_t prepack_scale_bytes(const PrepackDims& d) {
+  if (d.wf == WF_BF16) return 0;
+  size_t NKS = (d.K + KSTEP - 1) / KSTEP, NKG = (NKS + 3) / 4;
+  return (size_t)d.E1 * (d.N / 16) * NKG * 256;
+}
+
+hipError_t launch_prepack(const PrepackDims& d, const void* codes, const uint8_t* scales,
+                          void* codes_p, void* scales_p, hipStream_t st) {
+  size_t chunks = prepack_code_bytes(d) / 16;
+  dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
+  const uint8_t* src = (const uint8_t*)codes;
+  uint8_t* dst = (uint8_t*)codes_p;
+  if (d.wf == WF_FP8)
+    hipLaunchKernelGGL(k_prepack_codes<WF_FP8>, grid, block, 0, st, src, dst, d.E1, d.N, d.K, d.w13, d.I);
+  else if (d.wf == WF_FP4)
+    hipLaunchKernelGGL(k_prepack_codes<WF_FP4>, grid, block, 0, st, src, dst, d.E1, d.N, d.K, d.w13, d.I);
+  else
+    hipLaunchKernelGGL(k_prepack_codes<WF_BF16>, grid, block, 0, st, src, dst, d.E1, d.N, d.K, d.w13, d.I);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || d.wf == WF_BF16) return err;
+  size_t words = prepack_scale_bytes(d) / 4;
+  hipLaunchKernelGGL(k_prepack_scales, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                     scales, (uint32_t*)scales_p, d.E1, d.N, d.K, d.w13, d.I);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

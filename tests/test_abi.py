@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point include/mxmoe.h
+declares, and rejects bad arguments on the host (before any HIP call) with the documented codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mx_quantized_grouped_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from mx_quantized_grouped_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "mxmoe.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxmoe_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(B.status_string(s), str) and B.status_string(s)
+
+
+def test_route_validation(L):
+    r = L.mxmoe_route
+    assert r(None, 4, 8, 9, 0, None, None, None) == B.MXMOE_EINVAL        # k > E
+    assert r(None, 4, 8, 0, 0, None, None, None) == B.MXMOE_EINVAL        # k < 1
+    assert r(None, -1, 8, 2, 0, None, None, None) == B.MXMOE_EINVAL       # T < 0
+    assert r(None, 4, 2000, 2, 0, None, None, None) == B.MXMOE_EINVAL     # E too large
+    assert r(None, 4, 128, 64, 0, None, None, None) == B.MXMOE_EUNSUPPORTED
+    assert r(None, 4, 8, 2, 5, None, None, None) == B.MXMOE_EINVAL        # bad dtype
+    assert r(None, 4, 8, 2, 0, None, None, None) == B.MXMOE_EINVAL        # null pointers
+    assert r(None, 0, 8, 2, 0, None, None, None) == B.MXMOE_OK            # T = 0 no-op
+    assert r(ctypes.c_void_p(3), 4, 8, 2, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
+             None) == B.MXMOE_EINVAL                                     # misaligned fp32
+
+
+def test_align_validation_and_capacity(L):
+    assert L.mxmoe_align_capacity(3, 2, 1, 2) == 0                       # block_m not allowed
+    # S = 6 slots, at most min(E+1, S) = 3 touched experts: 6 + 3*15 = 51, rounded up to 16 -> 64
+    assert L.mxmoe_align_capacity(3, 2, 1, 16) == 64
+    assert L.mxmoe_align(None, 3, 2, 1, 20, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
+    assert L.mxmoe_align(None, 0, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_OK
+    assert L.mxmoe_align(None, 3, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
+    # large variant needs scratch
+    assert L.mxmoe_align_workspace_bytes(8192, 128, 8, 64) > 0
+    p = ctypes.c_void_p(256)
+    assert L.mxmoe_align(p, 8192, 128, 8, 64, p, p, p, None, None, 0, None) == B.MXMOE_EWORKSPACE
+
+
+def test_capacity_formula(L):
+    for T, E, k, bm in [(32, 128, 8, 16), (8192, 128, 8, 64), (1, 512, 8, 128), (6, 512, 8, 256)]:
+        S = T * (k + 1)
+        cap = S + min(E + 1, S) * (bm - 1)
+        assert L.mxmoe_align_capacity(T, E, k, bm) == -(-cap // bm) * bm
+
+
+def test_quantize_validation(L):
+    q = L.mxmoe_quantize
+    p = ctypes.c_void_p(256)
+    assert q(p, 4, 33, 0, 2, p, p, None) == B.MXMOE_EINVAL                # K % 32
+    assert q(p, 4, 64, 7, 2, p, p, None) == B.MXMOE_EINVAL                # src dtype
+    assert q(p, 4, 64, 0, 0, p, p, None) == B.MXMOE_EINVAL                # fmt
+    assert q(None, 4, 64, 0, 2, p, p, None) == B.MXMOE_EINVAL
+    assert q(ctypes.c_void_p(8), 4, 64, 0, 2, p, p, None) == B.MXMOE_EINVAL  # misaligned
+    assert q(None, 0, 64, 0, 2, None, None, None) == B.MXMOE_OK
+
+
+def test_shape_validation_and_sizes(L):
+    ok = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
+    assert B.mxmoe_workspace_bytes(ok) > 0
+    bad = [B.Shape.of(32, 3000, 128, 8, 384), B.Shape.of(32, 3072, 128, 8, 380),
+           B.Shape.of(32, 3072, 128, 0, 384), B.Shape.of(32, 3072, 128, 129, 384),
+           B.Shape(32, 3072, 128, 8, 384, 2, 0, 0), B.Shape(32, 3072, 128, 8, 384, 0, 2, 0),
+           B.Shape(32, 3072, 128, 8, 384, 9, 2, 0), B.Shape(32, 3072, 128, 8, 384, 2, 2, 4)]
+    for s in bad:
+        assert B.mxmoe_workspace_bytes(s) == 0
+        assert L.mxmoe_forward(ctypes.byref(s), None, None, None, None, None, None, None, None, 0,
+                               None) < 0
+    # H % 128 != 0 (but % 32 == 0) is a valid shape the kernels do not cover
+    assert L.mxmoe_forward(ctypes.byref(B.Shape.of(4, 160, 8, 2, 64)), None, None, None, None,
+                           None, None, None, None, 0, None) == B.MXMOE_EUNSUPPORTED
+    # prepacked sizes: fragment-major layout holds exactly the canonical bytes when K % 128 == 0
+    E1, H, I = 129, 3072, 384
+    assert B.mxmoe_prepacked_bytes(ok, 0) == E1 * 2 * I * H
+    assert B.mxmoe_prepacked_bytes(ok, 1) == E1 * 2 * I * H // 32
+    assert B.mxmoe_prepacked_bytes(ok, 2) == E1 * H * I
+    # scale dwords cover groups of four 128-K steps: I = 384 is 3 steps -> one (padded) group
+    assert B.mxmoe_prepacked_bytes(ok, 3) == E1 * (H // 16) * 1 * 256
+    f4 = B.Shape.of(128, 3072, 128, 8, 768, "mxfp4")
+    assert B.mxmoe_prepacked_bytes(f4, 0) == E1 * 2 * 768 * 3072 // 2
+    bf = B.Shape.of(16, 256, 8, 2, 128, "bf16")
+    assert B.mxmoe_prepacked_bytes(bf, 1) == 0 and B.mxmoe_prepacked_bytes(bf, 0) == 9 * 256 * 256 * 2
+    pad = B.Shape.of(4, 256, 4, 2, 96, "mxfp8")       # K of down padded 96 -> 128
+    assert B.mxmoe_prepacked_bytes(pad, 2) == 5 * 256 * 128
+
+
+def test_forward_workspace_checks(L):
+    s = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
+    need = B.mxmoe_workspace_bytes(s)
+    p = ctypes.c_void_p(4096)
+    args = [p] * 7
+    assert L.mxmoe_forward(ctypes.byref(s), *args, p, need - 1, None) == B.MXMOE_EWORKSPACE
+    assert L.mxmoe_forward(ctypes.byref(s), *args, ctypes.c_void_p(4096 + 64), need,
+                           None) == B.MXMOE_EWORKSPACE                   # misaligned
+    assert L.mxmoe_forward(ctypes.byref(s), *args[:6], None, p, need, None) == B.MXMOE_EINVAL
+    o = B.Options(3, 0, 0, 0)
+    assert B.mxmoe_workspace_bytes(s, o) == 0
+    o = B.Options(0, 0, 48, 0)
+    assert B.mxmoe_workspace_bytes(s, o) == 0
+
+
+def test_workspace_view(L):
+    s = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
+    off0, nb0, bm = B.mxmoe_workspace_view(s, None, B.VIEW_TOPK_IDS)
+    assert off0 == 0 and nb0 == 32 * 9 * 4 and bm == 16
+    off, nb, bm = B.mxmoe_workspace_view(s, B.Options(2, 2, 128, 0), B.VIEW_SORTED_IDS)
+    assert bm == 128 and nb == 4 * L.mxmoe_align_capacity(32, 128, 8, 128)
+    assert off % 256 == 0
+    with pytest.raises(B.MxMoeError):
+        B.mxmoe_workspace_view(s, None, 9)
