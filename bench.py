@@ -1,0 +1,294 @@
+"""Throughput of the MX MoE expert block on one MI355X, against the HBM / MFMA roofline.
+
+One step = one mxmoe_forward call (route -> align -> MXFP8 quant -> gate_up + SwiGLU + requant ->
+down + weighted combine -> bf16) over one batch of seeded synthetic input already resident in HBM.
+Weights rotate through several device copies (together more than twice the 256 MB last-level
+cache), so every step streams its expert weights from HBM as a serving loop does between calls of
+the same layer; the cold-weight effect is the microbenchmark pitfall of "Ling-3.0-flash: Tối ưu hóa
+độ trễ giải mã lên 54% trên 4 GPU Blackwell" ("Sửa thước đo trước khi sửa máy").
+
+Prints one JSON line. `value` is the headline workload's algorithmic HBM throughput (GB/s) at
+decode M; per-workload TFLOP/s, GB/s and roofline fractions (decode and prefill M) are in
+`workloads`. `roofline` is for the dominant kernel (gate_up), timed with HIP events that the
+library records on its own stream at stage boundaries. `cpu_baseline` is the fp64 CPU oracle on a
+bounded sample of the headline workload (host cores of the same machine)."""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+PEAK_MFMA_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 5000.0, "bf16": 2500.0}   # dense; fp8-rate issue
+# for W4A8 (fp8 activations) — the fp4 rate (10.1 PF) needs both operands in 4 bits.
+LLC_BYTES = 256 << 20              # MALL (infinity cache)
+METRIC = "MoE-block TFLOP/s and HBM GB/s (% of MI355X roofline) at decode/prefill M"
+ELEM_BYTES = {"mxfp8": 1.0, "mxfp4": 0.5, "bf16": 2.0}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- work figures
+def expert_bytes(w, part="all"):
+    """Algorithmic bytes of one expert's weights (codes + E8M0 scales)."""
+    eb = ELEM_BYTES[w.w_fmt] + (0.0 if w.w_fmt == "bf16" else 1.0 / 32)
+    per = {"w13": 2 * w.I * w.H * eb, "w2": w.H * w.I * eb}
+    return per["w13"] + per["w2"] if part == "all" else per[part]
+
+
+def block_bytes(w, touched):
+    """Weights of the touched experts + x, logits and y (the block's own algorithmic traffic)."""
+    return touched * expert_bytes(w) + w.T * w.H * 2 + w.T * w.E * 2 + w.T * w.H * 2
+
+
+def gate_up_bytes(w, touched):
+    act = 1.0 + (0.0 if w.act_fmt == "bf16" else 1.0 / 32)
+    a_in = w.T * w.H * (2.0 if w.act_fmt == "bf16" else act)
+    h_out = w.slots * w.I * (2.0 if w.act_fmt == "bf16" else act)
+    return touched * expert_bytes(w, "w13") + a_in + h_out
+
+
+def block_flops(w):
+    return 6.0 * w.H * w.I * w.slots
+
+
+def gate_up_flops(w):
+    return 4.0 * w.H * w.I * w.slots
+
+
+# ----------------------------------------------------------------------------- GPU leg
+class GpuWorkload:
+    def __init__(self, name, copies=None, threads=16):
+        import torch
+        import workloads
+        from mx_quantized_grouped_amd import binding as B
+        from mx_quantized_grouped_amd.weights import ExpertLoader
+        self.torch, self.B = torch, B
+        self.w = w = workloads.get(name)
+        self.shape = B.Shape.of(w.T, w.H, w.E, w.top_k, w.I, w.w_fmt)
+        t0 = time.time()
+        loader = ExpertLoader(self.shape, "cuda")
+        workloads.draw_all_experts(w, threads=threads, callback=loader.add_expert)
+        packed = loader.finish()
+        torch.cuda.synchronize()
+        wbytes = sum(p.numel() for p in packed)
+        n = copies or max(2, math.ceil(2 * LLC_BYTES / wbytes) + 1)
+        self.packed = [packed] + [tuple(p.clone() for p in packed) for _ in range(n - 1)]
+        torch.cuda.synchronize()
+        log(f"{name}: weights {wbytes / 1e6:.1f} MB x {n} copies prepared in {time.time() - t0:.1f}s")
+        to_dev = lambda b: torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16)
+        self.xb, self.lb = workloads.draw_x(w), workloads.draw_logits(w)
+        self.x, self.logits = to_dev(self.xb), to_dev(self.lb)
+        self.y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+        self.ws = torch.empty(B.mxmoe_workspace_bytes(self.shape), dtype=torch.uint8, device="cuda")
+
+    def step(self, i, options=None):
+        self.B.mxmoe_forward(self.shape, self.x, self.logits, self.packed[i % len(self.packed)],
+                             y=self.y, workspace=self.ws, options=options)
+
+    def touched_experts(self):
+        B = self.B
+        off, nb, _ = B.mxmoe_workspace_view(self.shape, None, B.VIEW_TOPK_IDS)
+        ids = self.ws[off:off + nb].view(self.torch.int32)
+        return int(self.torch.unique(ids).numel())
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            self.step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+    def time_stages(self, steps):
+        """Average duration of each stage, from events the library records on its stream."""
+        torch, B = self.torch, self.B
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MXMOE_STAGE_EVENTS)]
+               for _ in range(steps)]
+        for row in evs:                  # materialise the underlying hipEvent_t handles
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        import ctypes
+        arrs = [(ctypes.c_void_p * B.MXMOE_STAGE_EVENTS)(*[e.cuda_event for e in row]) for row in evs]
+        for i in range(steps):
+            opt = B.Options(0, 0, 0, 0, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p)))
+            self.step(i, opt)
+        torch.cuda.synchronize()
+        out = {}
+        for s, name in enumerate(B.STAGES):
+            out[name] = float(np.mean([row[s].elapsed_time(row[s + 1]) for row in evs]))
+        return out
+
+
+def measure(name, steps, warmup):
+    g = GpuWorkload(name)
+    ms, wall_ms = g.time_steps(steps, warmup)
+    stages = g.time_stages(max(10, min(steps, 50)))
+    touched = g.touched_experts()
+    w = g.w
+    by = block_bytes(w, touched)
+    fl = block_flops(w)
+    res = {
+        "T": w.T, "H": w.H, "E": w.E, "top_k": w.top_k, "shared_experts": 1, "I": w.I,
+        "w_fmt": w.w_fmt, "act_fmt": w.act_fmt, "zipf": w.zipf, "touched_experts": touched,
+        "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "algorithmic_MB": by / 1e6, "GFLOP": fl / 1e9,
+        "GBps": by / (ms * 1e-3) / 1e9, "TFLOPs": fl / (ms * 1e-3) / 1e12,
+        "stage_ms": stages,
+    }
+    res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
+    res["mfma_frac"] = res["TFLOPs"] / PEAK_MFMA_TFLOPS[w.w_fmt]
+    gu_ms = stages["gate_up"]
+    decode = w.slots < 16 * (w.E + 1)
+    if decode:
+        ach = gate_up_bytes(w, touched) / (gu_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "gate_up", "bound": "hbm", "achieved": ach,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                           "bytes_per_launch": gate_up_bytes(w, touched)}
+    else:
+        ach = gate_up_flops(w) / (gu_ms * 1e-3) / 1e12
+        pk = PEAK_MFMA_TFLOPS[w.w_fmt]
+        res["roofline"] = {"kernel": "gate_up", "bound": "mfma", "achieved": ach, "peak": pk,
+                           "unit": "TFLOP/s", "frac": ach / pk, "flops_per_launch": gate_up_flops(w)}
+    log(f"{name}: {ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
+        f"{res['TFLOPs']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% MFMA), stages(us) "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
+    return g, res
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(g, n_tokens):
+    """The fp64 oracle on a bounded sample: n_tokens tokens of the same workload. Weight codes are
+    produced before the timed region (load-time work); the timed region is the block itself:
+    routing, sort, Q1, explicit per-expert MX dequantisation, fp64 GEMMs, SwiGLU, Q2, combine."""
+    import workloads
+    from oracle import moe, mx
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = g.w
+    toks = np.arange(min(n_tokens, w.T))
+    x = workloads.f32_from_bf16_bits(g.xb).astype(np.float64)
+    lg = workloads.f32_from_bf16_bits(g.lb).astype(np.float64)
+    ids, _ = moe.route(lg[toks], w.top_k)
+    need = sorted(set(ids.reshape(-1).tolist()))
+    el = {"mxfp8": "e4m3", "mxfp4": "e2m1"}.get(w.w_fmt)
+    coded = {}
+    for e in need:                                    # untimed: load-time quantisation
+        a, b = workloads.draw_expert(w, e)
+        coded[e] = (mx.quantize(a, el), mx.quantize(b, el)) if el else (a, b)
+
+    def get(e):
+        if not el:
+            return np.asarray(coded[e][0], np.float64), np.asarray(coded[e][1], np.float64)
+        (c13, s13), (c2, s2) = coded[e]
+        return mx.dequantize(c13, s13, el), mx.dequantize(c2, s2, el)
+    W = moe.ExpertWeights(w.E, w.H, w.I, w.w_fmt, get, cache=0)
+    t0 = time.perf_counter()
+    r = moe.moe_block(x[toks], lg[toks], W, w.top_k, w.act_fmt)
+    moe.align(r.ids, w.E, 16)
+    sec = time.perf_counter() - t0
+    by = len(need) * expert_bytes(w) + len(toks) * (4 * w.H + 2 * w.E)
+    y = g.y.float().cpu().numpy().astype(np.float64)[toks]
+    par = moe.parity_stats(y, r.y)
+    return {"value": by / sec / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": sec, "gflops": 6.0 * w.H * w.I * (w.top_k + 1) * len(toks) / sec / 1e9,
+            "sample": f"{len(toks)} of {w.T} tokens of {w.name} ({len(need)} experts touched); "
+                      f"fp64 numpy, same process and host",
+            "parity_vs_gpu_on_sample": par}
+
+
+def traffic_record(name, kernel_src):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(name)
+    if not rec:
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    return rec.get("bytes_per_launch") if rec.get("gemm_src_sha") == h else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_mxfp8")
+    ap.add_argument("--extra", default="prefill_mxfp8",
+                    help="comma-separated extra workloads, 'all', or 'none'")
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the block runs on one GPU's share of the tensor-parallel "
+              "shapes and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from mx_quantized_grouped_amd import binding as B
+    B.lib()
+    g, head = measure(args.workload, args.steps, args.warmup)
+    others = {}
+    extra = [] if args.extra == "none" else (
+        [n for n in workloads.WORKLOADS if n != args.workload] if args.extra == "all"
+        else [n for n in args.extra.split(",") if n and n != args.workload])
+    base = None if args.no_cpu_baseline else cpu_baseline(g, args.cpu_tokens)
+    del g
+    torch.cuda.empty_cache()
+    for n in extra:
+        gx, r = measure(n, max(10, args.steps // 2), max(3, args.warmup // 2))
+        others[n] = r
+        del gx
+        torch.cuda.empty_cache()
+    rl = dict(head["roofline"])
+    rl["traffic"] = traffic_record(args.workload,
+                                   os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"))
+    w = workloads.get(args.workload)
+    out = {
+        "metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"mxfp8": "mxfp8xmxfp8->f32", "mxfp4": "mxfp4xmxfp8->f32", "bf16": "bf16->f32"}[w.w_fmt],
+        "data": "synthetic (seeded draws; weights N(0,0.02) quantised on the GPU)",
+        "config": {"workload": args.workload, **{k: head[k] for k in
+                   ("T", "H", "E", "top_k", "shared_experts", "I", "w_fmt", "act_fmt", "zipf")},
+                   "parallelism": "single GPU (one TP share, all experts resident)"},
+        "tflops": head["TFLOPs"], "hbm_frac": head["hbm_frac"], "mfma_frac": head["mfma_frac"],
+        "touched_experts": head["touched_experts"], "stage_ms": head["stage_ms"],
+        "roofline": rl, "cpu_baseline": base,
+        "workloads": {n: {k: v for k, v in r.items() if k not in ("T", "H", "E", "top_k",
+                                                                  "shared_experts")}
+                      for n, r in others.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

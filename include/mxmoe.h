@@ -70,13 +70,18 @@ typedef struct {
   int32_t w_fmt, act_fmt, logits_dtype;
 } mxmoe_shape;
 
-/* Optional knobs for A/B runs and tests; all-zero = automatic. */
+/* Optional knobs for A/B runs, tests and timing; all-zero = automatic. */
 typedef struct {
   int32_t launcher; /* MXMOE_LAUNCH_* */
   int32_t combine;  /* MXMOE_COMBINE_* */
   int32_t block_m;  /* align tile height (16, 32, 64, 128, 256); 0 = the launcher's default */
-  int32_t reserved;
+  int32_t reserved; /* must be 0 */
+  /* Optional array of MXMOE_STAGE_EVENTS caller-created hipEvent_t (passed as void*), recorded on
+     the stream at the stage boundaries of mxmoe_forward_ex: before route, align, quant, gate_up,
+     down, finalize, and after finalize. NULL = no events. */
+  void** stage_events;
 } mxmoe_options;
+#define MXMOE_STAGE_EVENTS 7
 
 /* Host: static description of a status code. Never NULL. */
 const char* mxmoe_status_string(int status);

@@ -48,9 +48,14 @@ class Shape(ctypes.Structure):
                      self.logits_dtype)
 
 
+MXMOE_STAGE_EVENTS = 7
+STAGES = ("route", "align", "quant", "gate_up", "down", "finalize")
+
+
 class Options(ctypes.Structure):
     _fields_ = [("launcher", ctypes.c_int32), ("combine", ctypes.c_int32),
-                ("block_m", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class MxMoeError(RuntimeError):

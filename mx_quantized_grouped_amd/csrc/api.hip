@@ -72,8 +72,9 @@ struct Plan {
 int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   int rc = check_shape(s);
   if (rc) return rc;
-  mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0};
-  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 2) return MXMOE_EINVAL;
+  mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr};
+  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 2 || o.reserved)
+    return MXMOE_EINVAL;
   if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
   Plan& p = *P;
   p.T = s->T; p.H = s->H; p.E = s->E; p.k = s->top_k; p.I = s->I;
@@ -274,10 +275,18 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
             P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.large ? "large_m" : "small_m", P.bm,
             slots ? "slots" : "atomic");
 
-  hipError_t e = launch_route(logits, s->logits_dtype == MXMOE_F32, P.T, P.E, P.k, ids, tw, st);
+  void** ev = opt ? opt->stage_events : nullptr;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_route(logits, s->logits_dtype == MXMOE_F32, P.T, P.E, P.k, ids, tw, st);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_align(ids, P.T, P.E, P.k, P.bm, sorted, bexp, counters, eoff, touched,
                      counters + 1, aws, st);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
     if (P.mx)
       e = launch_quantize_act((const uint16_t*)x, P.T, P.H, xq, xs, P.srs_H,
@@ -306,6 +315,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.topk_w = tw;
   g.out32 = out32;
   g.combine = P.combine;
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) {
     GemmParams gu = g;
     gu.a = P.mx ? xq : (const uint8_t*)x;
@@ -319,6 +329,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.NKG = (gu.NKS + 3) / 4;
     e = launch_gate_up(P.wf, P.large, gu, grid_y, st);
   }
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) {
     GemmParams dn = g;
     dn.a = h;
@@ -332,7 +343,9 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.NKG = (dn.NKS + 3) / 4;
     e = launch_down(P.wf, P.large, dn, grid_y, st);
   }
+  if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, slots, (uint16_t*)y, st);
+  if (e == hipSuccess) e = mark(6);
   return hip_status(e);
 }
 
