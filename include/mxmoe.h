@@ -77,11 +77,12 @@ typedef struct {
   int32_t block_m;  /* align tile height (16, 32, 64, 128, 256); 0 = the launcher's default */
   int32_t reserved; /* must be 0 */
   /* Optional array of MXMOE_STAGE_EVENTS caller-created hipEvent_t (passed as void*), recorded on
-     the stream at the stage boundaries of mxmoe_forward_ex: before route, align, quant, gate_up,
-     down, finalize, and after finalize. NULL = no events. */
+     the stream at the stage boundaries of mxmoe_forward_ex: before the prologue (routing, sort and
+     activation quantisation), before gate_up, before down, before the final bf16 rounding, and
+     after it. NULL = no events. */
   void** stage_events;
 } mxmoe_options;
-#define MXMOE_STAGE_EVENTS 7
+#define MXMOE_STAGE_EVENTS 5
 
 /* Host: static description of a status code. Never NULL. */
 const char* mxmoe_status_string(int status);

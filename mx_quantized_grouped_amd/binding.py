@@ -48,8 +48,8 @@ class Shape(ctypes.Structure):
                      self.logits_dtype)
 
 
-MXMOE_STAGE_EVENTS = 7
-STAGES = ("route", "align", "quant", "gate_up", "down", "finalize")
+MXMOE_STAGE_EVENTS = 5
+STAGES = ("prologue", "gate_up", "down", "finalize")
 
 
 class Options(ctypes.Structure):

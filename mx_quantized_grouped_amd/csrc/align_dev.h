@@ -1,0 +1,197 @@
+// Device side of moe_align: stable counting sort of the T*(k+1) routing slots into
+// expert-contiguous, tile-padded runs — the work list of the grouped GEMMs (grouped MoE programs
+// in "Lần theo điểm nghẽn: Tối ưu MiniMax M3 trên AMD Instinct MI355X", local-shapes passage). All
+// counts stay on the device; the host only knows the capacity bound (the batch-1 decode page
+// "Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell", "Hình dạng của một
+// bước batch-1": fixed shapes plus padding turn counts into GPU-side indices).
+//
+// Stable ranks are computed 1024 slots at a time: inside a wavefront, lanes holding the same expert
+// find each other with ballots (one ballot per distinct expert in the wave), and per-wave counts in
+// LDS give the offset contributed by the earlier waves.
+#pragma once
+#include "device.h"
+#include "kernels.h"
+
+namespace mxmoe {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kAlignMaxE1 = kMaxExperts + 1;  // routed + shared; the block scans take two per thread
+
+// LDS of the single-workgroup sort. Per-wave counts (ballot variant) or one bit per slot per
+// expert (bitmap variant) share the same space.
+constexpr int kAlignBitmapWords = kAlignWaves * kAlignMaxE1 * 2 / 8;
+struct AlignSmem {
+  int cnt[kAlignMaxE1];
+  int off[kAlignMaxE1 + 1];
+  int run[kAlignMaxE1];
+  union {
+    uint16_t wcnt[kAlignWaves][kAlignMaxE1];
+    unsigned long long bits[kAlignBitmapWords];
+  };
+  int s_wave[kAlignWaves];
+};
+
+// Mask of the lanes of this wave whose key equals this lane's key (valid lanes only).
+__device__ __forceinline__ uint64_t match_peers(int key, bool valid) {
+  uint64_t todo = __ballot(valid);
+  uint64_t mine = 0;
+  while (todo) {
+    int leader = __ffsll((unsigned long long)todo) - 1;
+    int kl = __shfl(key, leader);
+    bool same = valid && key == kl;
+    uint64_t m = __ballot(same);
+    if (same) mine = m;
+    todo &= ~m;
+  }
+  return mine;
+}
+
+// Exclusive scan over the 1024-thread workgroup (one value each); also returns the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kAlignWaves; ++i) {
+    int s = s_wave[i];
+    before += i < wave ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int align_expert_of(const int32_t* ids, int f, int S, int E1) {
+  if (f >= S) return -1;
+  int e = ids[f];
+  return (e >= 0 && e < E1) ? e : -1;  // out-of-range ids are dropped
+}
+
+// From per-expert counts cnt[0..E1): padded offsets off[0..E1], the touched-expert list and all
+// layout outputs except the scatter of valid slots. Called by the whole 1024-thread workgroup.
+inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1, int S, int bm, int cap,
+                                         int* s_wave, const AlignOut& o) {
+  const int t = threadIdx.x;
+  const int e0 = 2 * t, e1 = 2 * t + 1;
+  int c0 = e0 < E1 ? cnt[e0] : 0, c1 = e1 < E1 ? cnt[e1] : 0;
+  int p0 = (c0 + bm - 1) / bm * bm, p1 = (c1 + bm - 1) / bm * bm;
+  int total;
+  int ex = block_excl_scan(p0 + p1, s_wave, &total);
+  if (e0 < E1) off[e0] = ex;
+  if (e1 < E1) off[e1] = ex + p0;
+  int ntouch;
+  int tx = block_excl_scan((c0 > 0) + (c1 > 0), s_wave, &ntouch);
+  if (o.touched) {
+    if (c0 > 0) o.touched[tx] = e0;
+    if (c1 > 0) o.touched[tx + (c0 > 0)] = e1;
+  }
+  if (t == 0) {
+    off[E1] = total;
+    *o.num_post_pad = total;
+    if (o.n_touched) *o.n_touched = ntouch;
+  }
+  __syncthreads();
+  if (o.expert_off)
+    for (int e = t; e <= E1; e += kAlignThreads) o.expert_off[e] = off[e];
+  // padding of each expert's run, then the unused tail
+  for (int e = t; e < E1; e += kAlignThreads)
+    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) o.sorted_ids[r] = S;
+  for (int r = total + t; r < cap; r += kAlignThreads) o.sorted_ids[r] = S;
+  // expert of every tile: binary search of the tile start in off[]
+  const int nb = cap / bm;
+  for (int b = t; b < nb; b += kAlignThreads) {
+    int pos = b * bm, v = -1;
+    if (pos < total) {
+      int lo = 0, hi = E1 - 1;  // largest e with off[e] <= pos: the non-empty run holding pos
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      v = lo;
+    }
+    o.block_expert[b] = v;
+  }
+}
+
+// The whole sort in one 1024-thread workgroup (S small). ids may live in LDS or global memory.
+// When E1 * ceil(S / 64) words fit, every expert gets an S-bit set of its slots: the stable rank
+// of slot f is the number of set bits below f (popcounts), and the count is the total — no ballot
+// loop. Otherwise ranks come from wave ballots and per-wave counts.
+inline __device__ void align_small_body(const int32_t* ids, int S, int E1, int bm, int cap,
+                                        const AlignOut& o, AlignSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int words = (S + 63) >> 6;
+  if (E1 * words <= kAlignBitmapWords) {
+    for (int i = t; i < E1 * words; i += kAlignThreads) sm.bits[i] = 0ull;
+    __syncthreads();
+    for (int f = t; f < S; f += kAlignThreads) {
+      int e = align_expert_of(ids, f, S, E1);
+      if (e >= 0) atomicOr(&sm.bits[e * words + (f >> 6)], 1ull << (f & 63));
+    }
+    __syncthreads();
+    for (int e = t; e < E1; e += kAlignThreads) {
+      int c = 0;
+      for (int w = 0; w < words; ++w) c += __popcll(sm.bits[e * words + w]);
+      sm.cnt[e] = c;
+    }
+    __syncthreads();
+    align_layout_from_counts(sm.cnt, sm.off, E1, S, bm, cap, sm.s_wave, o);
+    __syncthreads();
+    for (int f = t; f < S; f += kAlignThreads) {
+      int e = align_expert_of(ids, f, S, E1);
+      if (e < 0) continue;
+      const unsigned long long* b = sm.bits + e * words;
+      int rank = __popcll(b[f >> 6] & ((1ull << (f & 63)) - 1ull));
+      for (int w = 0; w < (f >> 6); ++w) rank += __popcll(b[w]);
+      o.sorted_ids[sm.off[e] + rank] = f;
+    }
+    return;
+  }
+  for (int e = t; e < E1; e += kAlignThreads) {
+    sm.cnt[e] = 0;
+    sm.run[e] = 0;
+    for (int w = 0; w < kAlignWaves; ++w) sm.wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  for (int f = t; f < S; f += kAlignThreads) {
+    int e = align_expert_of(ids, f, S, E1);
+    if (e >= 0) atomicAdd(&sm.cnt[e], 1);
+  }
+  __syncthreads();
+  align_layout_from_counts(sm.cnt, sm.off, E1, S, bm, cap, sm.s_wave, o);
+  __syncthreads();
+  for (int base = 0; base < S; base += kAlignThreads) {
+    int f = base + t;
+    int e = align_expert_of(ids, f, S, E1);
+    uint64_t peers = match_peers(e, e >= 0);
+    int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (e >= 0 && rank == 0) sm.wcnt[wave][e] = (uint16_t)__popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += sm.wcnt[w][e];
+      o.sorted_ids[sm.off[e] + sm.run[e] + before + rank] = f;
+    }
+    __syncthreads();
+    for (int x = t; x < E1; x += kAlignThreads) {
+      int s = 0;
+      for (int w = 0; w < kAlignWaves; ++w) {
+        s += sm.wcnt[w][x];
+        sm.wcnt[w][x] = 0;
+      }
+      sm.run[x] += s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace mxmoe

@@ -280,21 +280,24 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_route(logits, s->logits_dtype == MXMOE_F32, P.T, P.E, P.k, ids, tw, st);
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = launch_align(ids, P.T, P.E, P.k, P.bm, sorted, bexp, counters, eoff, touched,
-                     counters + 1, aws, st);
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) {
-    if (P.mx)
-      e = launch_quantize_act((const uint16_t*)x, P.T, P.H, xq, xs, P.srs_H,
-                              slots ? nullptr : out32, st);
-    else if (!slots)
-      e = launch_zero_f32(out32, (size_t)P.T * P.H, st);
-  }
-  const int grid_y = P.large ? P.cap / P.bm : (P.E1 < P.S ? P.E1 : P.S);
+  PrologueArgs pa;
+  pa.logits = logits;
+  pa.T = P.T;
+  pa.E = P.E;
+  pa.top_k = P.k;
+  pa.ids = ids;
+  pa.w = tw;
+  pa.block_m = P.bm;
+  pa.cap = P.cap;
+  pa.out = AlignOut{sorted, bexp, counters, eoff, touched, counters + 1};
+  pa.x = (const uint16_t*)x;
+  pa.H = P.H;
+  pa.xq = P.mx ? xq : nullptr;
+  pa.xs = xs;
+  pa.srs = P.srs_H;
+  pa.zero_out = slots ? nullptr : out32;
+  if (e == hipSuccess) e = launch_prologue(pa, s->logits_dtype == MXMOE_F32, aws, st);
+  const int n_blocks = P.cap / P.bm;
   GemmParams g{};
   g.sorted_ids = sorted;
   g.expert_off = eoff;
@@ -315,37 +318,41 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.topk_w = tw;
   g.out32 = out32;
   g.combine = P.combine;
-  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
     gu.a = P.mx ? xq : (const uint8_t*)x;
     gu.as = xs;
     gu.a_stride = P.mx ? P.H : 2 * P.H;
     gu.a_srs = P.srs_H;
+    gu.a_bytes = (uint32_t)((size_t)P.T * gu.a_stride);
+    gu.as_bytes = (uint32_t)((size_t)P.T * P.srs_H);
     gu.w = (const uint8_t*)w13_p;
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
     gu.NKG = (gu.NKS + 3) / 4;
-    e = launch_gate_up(P.wf, P.large, gu, grid_y, st);
+    e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
-  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) {
     GemmParams dn = g;
     dn.a = h;
     dn.as = hs;
     dn.a_stride = g.h_stride;
     dn.a_srs = P.srs_I;
+    dn.a_bytes = (uint32_t)((size_t)P.cap * dn.a_stride);
+    dn.as_bytes = (uint32_t)((size_t)P.cap * P.srs_I);
     dn.w = (const uint8_t*)w2_p;
     dn.ws = (const uint8_t*)s2_p;
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
     dn.NKG = (dn.NKS + 3) / 4;
-    e = launch_down(P.wf, P.large, dn, grid_y, st);
+    e = launch_down(P.wf, P.large, dn, n_blocks, st);
   }
-  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, slots, (uint16_t*)y, st);
-  if (e == hipSuccess) e = mark(6);
+  if (e == hipSuccess) e = mark(4);
   return hip_status(e);
 }
 

@@ -16,11 +16,37 @@ hipError_t launch_route(const void* logits, bool logits_f32, int T, int E, int t
                         int32_t* ids, float* w, hipStream_t st);
 
 // align.hip
+struct AlignOut {
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_post_pad;
+  int32_t* expert_off;  // may be null
+  int32_t* touched;     // may be null
+  int32_t* n_touched;   // may be null
+};
 size_t align_scratch_bytes(int T, int E, int top_k);
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
                         int32_t* expert_off, int32_t* touched, int32_t* n_touched, void* scratch,
                         hipStream_t st);
+
+// prologue.hip: route + sort + activation quantisation (or accumulator clearing) for forward.
+struct PrologueArgs {
+  const void* logits;
+  int T, E, top_k;
+  int32_t* ids;
+  float* w;
+  int block_m, cap;
+  AlignOut out;
+  const uint16_t* x;
+  int H;
+  uint8_t* xq;      // null: no quantisation (bf16 path)
+  uint8_t* xs;
+  int srs;
+  float* zero_out;  // null: nothing to clear
+};
+hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_scratch,
+                           hipStream_t st);
 
 // quant.hip
 // Canonical MX quantisation (codes row-major, scales [rows, K/32]).
@@ -52,6 +78,8 @@ struct GemmParams {
   const uint8_t* as;         // A kernel-native scales (MX)
   int a_stride;              // bytes per A row
   int a_srs;                 // bytes per A scale row
+  uint32_t a_bytes;          // size of the A matrix (rows * a_stride), < 2 GiB
+  uint32_t as_bytes;         // size of the A scale matrix
   const uint8_t* w;          // prepacked weights
   const uint8_t* ws;         // prepacked weight scales (MX)
   int NT, NKS, NKG;          // per expert: 16-row N tiles, K-steps of 128, groups of 4 K-steps

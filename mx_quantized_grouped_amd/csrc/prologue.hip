@@ -1,0 +1,95 @@
+// Fused front of the block: routing, the sort and the activation quantisation in as few launches
+// as the batch allows. Launch count matters at decode sizes, where every kernel node costs a few
+// microseconds ("Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell",
+// "Hai loại thời gian nhàn rỗi": hundreds of 1.5-6 us kernel nodes at batch 1).
+//   small batches (S <= 4096): one launch; workgroup 0 routes every token (one wave per token) into
+//     LDS and sorts the slots there, the other workgroups quantise x (and clear the atomic
+//     accumulator when that combine is used).
+//   larger batches: one launch routes and quantises, then the three-pass sort.
+#include "align_dev.h"
+#include "device.h"
+#include "kernels.h"
+#include "quant_dev.h"
+#include "route_dev.h"
+
+namespace mxmoe {
+
+namespace {
+
+constexpr int kThreads = 1024;
+
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
+  if (blockIdx.x == 0) {
+    __shared__ AlignSmem sm;
+    __shared__ int32_t ids_lds[kAlignSmallMaxSlots];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    route_tokens_any<F32>(a.logits, wave, kThreads / 64, a.T, a.E, a.top_k, lane, a.ids, a.w,
+                          ids_lds);
+    __syncthreads();
+    align_small_body(ids_lds, a.T * (a.top_k + 1), a.E + 1, a.block_m, a.cap, a.out, sm);
+    return;
+  }
+  const size_t blk = (size_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
+  const int nbk = a.H / 32;
+  if (blk >= (size_t)a.T * nbk) return;
+  const size_t t = blk / nbk;
+  const int kb = (int)(blk - t * nbk);
+  if (a.xq) {
+    quant_act_block(a.x, t, kb, a.H, a.xq, a.xs, a.srs, a.zero_out);
+  } else if (a.zero_out) {
+    v4f* z = (v4f*)(a.zero_out + t * a.H + (size_t)kb * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Larger batches: workgroups [0, n_route) route 16 tokens each; the rest quantise / clear.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_route) {
+  if ((int)blockIdx.x < n_route) {
+    const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (t < a.T)
+      route_tokens_any<F32>(a.logits, t, a.T, a.T, a.E, a.top_k, threadIdx.x & 63, a.ids, a.w,
+                            nullptr);
+    return;
+  }
+  const size_t blk = (size_t)(blockIdx.x - n_route) * kThreads + threadIdx.x;
+  const int nbk = a.H / 32;
+  if (blk >= (size_t)a.T * nbk) return;
+  const size_t t = blk / nbk;
+  const int kb = (int)(blk - t * nbk);
+  if (a.xq) {
+    quant_act_block(a.x, t, kb, a.H, a.xq, a.xs, a.srs, a.zero_out);
+  } else if (a.zero_out) {
+    v4f* z = (v4f*)(a.zero_out + t * a.H + (size_t)kb * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_scratch,
+                           hipStream_t st) {
+  const int S = a.T * (a.top_k + 1);
+  const bool work = a.xq || a.zero_out;
+  const int nq = work ? (int)(((size_t)a.T * (a.H / 32) + kThreads - 1) / kThreads) : 0;
+  if (S <= kAlignSmallMaxSlots) {
+    dim3 grid(1 + nq), block(kThreads);
+    if (logits_f32) hipLaunchKernelGGL(k_prologue_small<true>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(k_prologue_small<false>, grid, block, 0, st, a);
+    return hipGetLastError();
+  }
+  const int nr = (a.T + kThreads / 64 - 1) / (kThreads / 64);
+  dim3 grid(nr + nq), block(kThreads);
+  if (logits_f32) hipLaunchKernelGGL(k_route_quant<true>, grid, block, 0, st, a, nr);
+  else hipLaunchKernelGGL(k_route_quant<false>, grid, block, 0, st, a, nr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_align(a.ids, a.T, a.E, a.top_k, a.block_m, a.out.sorted_ids, a.out.block_expert,
+                      a.out.num_post_pad, a.out.expert_off, a.out.touched, a.out.n_touched,
+                      align_scratch, st);
+}
+
+}  // namespace mxmoe

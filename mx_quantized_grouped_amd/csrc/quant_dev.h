@@ -1,0 +1,80 @@
+// Device side of MX quantisation (see quant.hip for the rule). One thread handles one block of 32
+// consecutive values.
+#pragma once
+#include "device.h"
+
+namespace mxmoe {
+
+// Load 32 consecutive source elements as fp32.
+template <bool F32>
+__device__ __forceinline__ void load32(const void* src, size_t off, float* v) {
+  if (F32) {
+    const v4f* p = (const v4f*)((const float*)src + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v4f q = p[i];
+      v[4 * i] = q[0]; v[4 * i + 1] = q[1]; v[4 * i + 2] = q[2]; v[4 * i + 3] = q[3];
+    }
+  } else {
+    const v4i* p = (const v4i*)((const uint16_t*)src + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v4i q = p[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t u = (uint32_t)q[j];
+        v[8 * i + 2 * j] = __uint_as_float(u << 16);
+        v[8 * i + 2 * j + 1] = __uint_as_float(u & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float amax32(const float* v) {
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  return a;
+}
+
+// 32 E4M3 codes packed little-endian into 8 dwords.
+__device__ __forceinline__ void encode_fp8_32(const float* v, int se, uint32_t* out) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    out[i] = e4m3_code(v[4 * i], se) | (e4m3_code(v[4 * i + 1], se) << 8) |
+             (e4m3_code(v[4 * i + 2], se) << 16) | (e4m3_code(v[4 * i + 3], se) << 24);
+}
+// 32 E2M1 codes, element 2i in the low nibble of byte i, packed into 4 dwords.
+__device__ __forceinline__ void encode_fp4_32(const float* v, int se, uint32_t* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d |= e2m1_code(v[8 * i + j], se) << (4 * j);
+    out[i] = d;
+  }
+}
+
+// Activation block (t, kb) of bf16 x [T, H] -> E4M3 codes in xq [T, H] and the kernel-native scale
+// byte in xs [T, srs]; optionally clears the matching 32 floats of zero_out [T, H].
+__device__ __forceinline__ void quant_act_block(const uint16_t* x, size_t t, int kb, int H,
+                                                uint8_t* xq, uint8_t* xs, int srs,
+                                                float* zero_out) {
+  size_t off = t * H + (size_t)kb * 32;
+  float v[32];
+  load32<false>(x, off, v);
+  int se = mx_shared_exp<8>(amax32(v));
+  xs[t * srs + act_scale_byte(kb)] = (uint8_t)(se + 127);
+  uint32_t o[8];
+  encode_fp8_32(v, se, o);
+  v4i* p = (v4i*)(xq + off);
+  p[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  p[1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+  if (zero_out) {
+    v4f* z = (v4f*)(zero_out + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+}  // namespace mxmoe

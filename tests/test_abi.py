@@ -130,7 +130,7 @@ def test_forward_workspace_checks(L):
 def test_workspace_view(L):
     s = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
     off0, nb0, bm = B.mxmoe_workspace_view(s, None, B.VIEW_TOPK_IDS)
-    assert off0 == 0 and nb0 == 32 * 9 * 4 and bm == 16
+    assert off0 == 0 and nb0 == 32 * 9 * 4 and bm == 16   # small-M default tile: 16 rows
     off, nb, bm = B.mxmoe_workspace_view(s, B.Options(2, 2, 128, 0), B.VIEW_SORTED_IDS)
     assert bm == 128 and nb == 4 * L.mxmoe_align_capacity(32, 128, 8, 128)
     assert off % 256 == 0
