@@ -58,9 +58,12 @@ enum {
 
 /* Launcher choice (small-M = expert-major decode grid, large-M = block-major prefill grid). */
 enum { MXMOE_LAUNCH_AUTO = 0, MXMOE_LAUNCH_SMALL_M = 1, MXMOE_LAUNCH_LARGE_M = 2 };
-/* Combine of the k+1 slot outputs of a token: per-slot rows summed in a fixed order
-   (deterministic) or fp32 atomics into a token-major accumulator (order varies run to run). */
-enum { MXMOE_COMBINE_AUTO = 0, MXMOE_COMBINE_SLOTS = 1, MXMOE_COMBINE_ATOMIC = 2 };
+/* Combine of the k+1 slot outputs of a token: per-slot fp32 rows summed in a fixed order
+   (deterministic), fp32 atomics into a token-major accumulator (order varies run to run), or
+   per-slot rows rounded to bf16 and summed in a fixed order (half the traffic of fp32 rows; one
+   extra rounding per slot). */
+enum { MXMOE_COMBINE_AUTO = 0, MXMOE_COMBINE_SLOTS = 1, MXMOE_COMBINE_ATOMIC = 2,
+       MXMOE_COMBINE_SLOTS_BF16 = 3 };
 
 /* Problem shape. Requirements: T >= 0; H % 128 == 0; I % 32 == 0; 1 <= top_k <= E <= 1024;
    w_fmt in {BF16, MXFP8_E4M3, MXFP4_E2M1}; act_fmt = MXFP8_E4M3 for MX weights and BF16 for bf16

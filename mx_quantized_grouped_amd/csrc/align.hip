@@ -43,29 +43,58 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
   }
 }
 
-// Pass 2 (one workgroup): totals, padded offsets, layout outputs, and hist turned in place into the
-// absolute start of each (chunk, expert) piece.
-__global__ __launch_bounds__(kAlignThreads) void k_align_scan(int32_t* hist, int nchunks, int S,
-                                                              int E1, int bm, int cap, AlignOut o) {
+// Pass 2 (one workgroup): totals, padded offsets and layout outputs; start[c * E1 + e] becomes the
+// absolute start of the (chunk c, expert e) piece. Threads split into (expert, segment of chunks)
+// pairs so the chunk histograms are walked in parallel.
+__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist,
+                                                              int32_t* __restrict__ start,
+                                                              int nchunks, int S, int E1, int bm,
+                                                              int cap, AlignOut o) {
   __shared__ int cnt[kAlignMaxE1];
   __shared__ int off[kAlignMaxE1 + 1];
   __shared__ int s_wave[kAlignWaves];
+  __shared__ int seg_sum[kAlignThreads];
   const int t = threadIdx.x;
-  for (int e = t; e < E1; e += kAlignThreads) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int v = hist[(size_t)c * E1 + e];
-      hist[(size_t)c * E1 + e] = s;  // exclusive prefix over chunks
-      s += v;
+  const int P = E1 >= kAlignThreads ? 1 : kAlignThreads / E1;  // segments per expert
+  const int seg = (nchunks + P - 1) / P;
+  const int part = t / E1, e = t - part * E1;
+  const bool mine = part < P;
+  int c_lo = 0, c_hi = 0;
+  if (mine) {
+    c_lo = part * seg;
+    c_hi = min(nchunks, c_lo + seg);
+  }
+  // experts beyond the first 1024 (E1 > 1024) are summed by a second pass of the same threads
+  for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
+    if (pass == 1 && (P != 1 || ee >= E1)) break;
+    int sum = 0;
+    if (mine && ee < E1)
+      for (int c = c_lo; c < c_hi; ++c) sum += hist[(size_t)c * E1 + ee];
+    if (pass == 0) seg_sum[t] = sum;
+    else cnt[ee] = sum;
+  }
+  __syncthreads();
+  for (int x = t; x < E1 && x < kAlignThreads; x += kAlignThreads) {
+    if (P == 1) { cnt[x] = seg_sum[x]; continue; }
+    int s2 = 0;
+    for (int q = 0; q < P; ++q) {
+      int v = seg_sum[q * E1 + x];
+      seg_sum[q * E1 + x] = s2;  // exclusive prefix over segments
+      s2 += v;
     }
-    cnt[e] = s;
+    cnt[x] = s2;
   }
   __syncthreads();
   align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o);
   __syncthreads();
-  for (int e = t; e < E1; e += kAlignThreads) {
-    int oe = off[e];
-    for (int c = 0; c < nchunks; ++c) hist[(size_t)c * E1 + e] += oe;
+  for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
+    if (pass == 1 && (P != 1 || ee >= E1)) break;
+    if (!mine || ee >= E1) continue;
+    int run = off[ee] + (P == 1 ? 0 : seg_sum[t]);
+    for (int c = c_lo; c < c_hi; ++c) {
+      start[(size_t)c * E1 + ee] = run;
+      run += hist[(size_t)c * E1 + ee];
+    }
   }
 }
 
@@ -92,7 +121,8 @@ size_t align_scratch_bytes(int T, int E, int top_k) {
   if (S <= (size_t)kAlignSmallMaxSlots) return 0;
   size_t nch = (S + kAlignChunk - 1) / kAlignChunk;
   size_t rank = (S * 4 + 255) / 256 * 256;
-  return rank + nch * (size_t)(E + 1) * 4;
+  size_t hist = (nch * (size_t)(E + 1) * 4 + 255) / 256 * 256;
+  return rank + 2 * hist;  // rank, chunk histograms, chunk starts
 }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
@@ -109,12 +139,14 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m
   }
   const int nch = (S + kAlignChunk - 1) / kAlignChunk;
   int32_t* rank = (int32_t*)scratch;
+  const size_t hist_bytes = ((size_t)nch * E1 * 4 + 255) / 256 * 256;
   int32_t* hist = (int32_t*)((char*)scratch + ((size_t)S * 4 + 255) / 256 * 256);
+  int32_t* start = (int32_t*)((char*)hist + hist_bytes);
   hipLaunchKernelGGL(k_align_count, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank, hist);
-  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, nch, S, E1, block_m,
-                     cap, o);
-  hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank, hist,
-                     sorted_ids);
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, start, nch, S, E1,
+                     block_m, cap, o);
+  hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank,
+                     start, sorted_ids);
   return hipGetLastError();
 }
 

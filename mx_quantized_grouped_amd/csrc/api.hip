@@ -73,7 +73,7 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   int rc = check_shape(s);
   if (rc) return rc;
   mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr};
-  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 2 || o.reserved)
+  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.reserved)
     return MXMOE_EINVAL;
   if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
   Plan& p = *P;
@@ -84,8 +84,10 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   // Launcher: block-major (large-M) once the average expert holds enough rows to fill tiles.
   p.large = o.launcher == MXMOE_LAUNCH_LARGE_M ||
             (o.launcher == MXMOE_LAUNCH_AUTO && p.S >= 16 * p.E1);
-  p.combine = o.combine ? o.combine : (p.large ? MXMOE_COMBINE_ATOMIC : MXMOE_COMBINE_SLOTS);
-  p.bm = o.block_m ? o.block_m : (p.large ? 64 : 16);
+  // Large batches write bf16 slot rows (fp32 atomics run at about one value per L2 channel per
+  // cycle, far below what the prefill combine needs); small batches keep fp32 slot rows.
+  p.combine = o.combine ? o.combine : (p.large ? MXMOE_COMBINE_SLOTS_BF16 : MXMOE_COMBINE_SLOTS);
+  p.bm = o.block_m ? o.block_m : (p.large ? (p.mx ? 128 : 64) : 16);
   p.cap = (int)cap_of(p.S, p.E1, p.bm);
   p.Ip = round_up(p.I, KSTEP);
   p.srs_H = scale_row_bytes(p.H);
@@ -103,7 +105,8 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   sz[SEG_XS] = p.mx ? (size_t)p.T * p.srs_H : 0;
   sz[SEG_H] = (size_t)p.cap * p.Ip * (p.mx ? 1 : 2);
   sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
-  sz[SEG_OUT] = (size_t)(p.combine == MXMOE_COMBINE_SLOTS ? p.S : p.T) * p.H * 4;
+  sz[SEG_OUT] = p.combine == MXMOE_COMBINE_ATOMIC ? (size_t)p.T * p.H * 4
+                                                  : (size_t)p.S * p.H * (p.combine == MXMOE_COMBINE_SLOTS ? 4 : 2);
   size_t at = 0;
   for (int i = 0; i < NSEG; ++i) {
     p.off[i] = at;
@@ -268,12 +271,12 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   uint8_t* h = (uint8_t*)(ws + P.off[SEG_H]);
   uint8_t* hs = (uint8_t*)(ws + P.off[SEG_HS]);
   float* out32 = (float*)(ws + P.off[SEG_OUT]);
-  const bool slots = P.combine == MXMOE_COMBINE_SLOTS;
+  const bool slots = P.combine != MXMOE_COMBINE_ATOMIC;
 
   if (getenv("MXMOE_TRACE"))
     fprintf(stderr, "mxmoe_forward: T=%d H=%d E=%d k=%d I=%d w=%d launcher=%s block_m=%d combine=%s\n",
             P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.large ? "large_m" : "small_m", P.bm,
-            slots ? "slots" : "atomic");
+            P.combine == 1 ? "slots" : (P.combine == 2 ? "atomic" : "slots_bf16"));
 
   void** ev = opt ? opt->stage_events : nullptr;
   auto mark = [&](int i) -> hipError_t {
@@ -351,7 +354,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     e = launch_down(P.wf, P.large, dn, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, slots, (uint16_t*)y, st);
+  if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, P.combine, (uint16_t*)y, st);
   if (e == hipSuccess) e = mark(4);
   return hip_status(e);
 }

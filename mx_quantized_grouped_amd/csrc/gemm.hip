@@ -101,8 +101,8 @@ __device__ __forceinline__ void tile_act_rows(const GemmParams& p, int m0, int r
   }
 }
 
-template <int WF, int MT>
-__device__ __forceinline__ void load_b(const GemmParams& p, const TileRows<MT>& tr, int ks,
+template <int WF, int MT, int MTR>
+__device__ __forceinline__ void load_b(const GemmParams& p, const TileRows<MTR>& tr, int ks,
                                        int lane, Stage<WF, MT>& s) {
   constexpr int FB = Frag<WF>::bytes;
 #pragma unroll
@@ -145,7 +145,7 @@ __device__ __forceinline__ void load_a(const TileRows<MT>& tr, int ks, Stage<WF,
 template <int WF, int MT>
 __device__ __forceinline__ void load_stage(const GemmParams& p, const TileRows<MT>& tr, int ks,
                                            int lane, Stage<WF, MT>& s) {
-  load_b<WF, MT>(p, tr, ks, lane, s);
+  load_b<WF, MT, MT>(p, tr, ks, lane, s);
   load_a<WF, MT>(tr, ks, s);
 }
 
@@ -228,6 +228,7 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
   }
 }
 
+// combine 1: fp32 slot rows [S, H]; 2: fp32 atomics into token rows [T, H]; 3: bf16 slot rows.
 template <int MT>
 __device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&acc)[MT][4], int m0,
                                               int r1, int chunk, int n, int g) {
@@ -240,9 +241,15 @@ __device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&a
       const int sid = p.sorted_ids[rr];
       if (sid >= p.S) continue;
       const float wt = p.topk_w[sid];
+      const int c0 = 64 * chunk + n;
+      if (p.combine == 3) {
+        uint16_t* orow = (uint16_t*)p.out32 + (size_t)sid * p.H;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) orow[c0 + 16 * f] = (uint16_t)f32_to_bf16_bits(wt * acc[mt][f][i]);
+        continue;
+      }
       float* orow = p.combine == 1 ? p.out32 + (size_t)sid * p.H
                                    : p.out32 + (size_t)(sid / p.k1) * p.H;
-      const int c0 = 64 * chunk + n;
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         float v = wt * acc[mt][f][i];
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     // is peeled. Weight loads of the first group go out before the (dependent) row lookup.
     Stage<WF, MT> buf[D];
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_b<WF, MT>(p, tr, s, lane, buf[s]);
+    for (int s = 0; s < D; ++s) load_b<WF, MT, MT>(p, tr, s, lane, buf[s]);
     tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
 #pragma unroll
     for (int s = 0; s < D; ++s) load_a<WF, MT>(tr, s, buf[s]);
@@ -301,6 +308,178 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
 }
 
 // ------------------------------------------------------------------------------ large-M
+// Prefill launcher: a workgroup of 4 waves computes a 128-row x 256-column tile (rows of one expert
+// from the sorted layout). The gathered activation tile of each 128-K step is staged through LDS
+// (double-buffered) and shared by the 4 waves; each wave streams its own 4 weight fragments (64
+// columns) into registers, one K-step ahead. Per K-step a wave issues 8 x 4 block-scaled MFMAs.
+// LDS rows are 128 bytes with the eight 16-byte column units of row r stored at unit c ^ (r & 7):
+// the 16 rows an MFMA operand read touches then spread over all banks (measured on gfx950: ~198
+// B/clk/CU for this read pattern, against ~119 with 16-byte row padding).
+constexpr int kTileM = 128;
+constexpr int kTileWaves = 4;
+constexpr int kLdsPitch = KSTEP;
+__device__ __forceinline__ int lds_unit(int row, int c) { return (c ^ (row & 7)) << 4; }
+
+template <int WF, bool GATE_UP, int P>
+__global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
+  constexpr int MT = kTileM / 16;
+  // per buffer: the 128 x 128-byte activation tile, then the tile's scale bytes for the K-step's
+  // group (16 bytes per row: the four lane-group dwords of the kernel-native scale layout)
+  constexpr int kTileBytes = kTileM * kLdsPitch;
+  constexpr int kBufBytes = kTileBytes + kTileM * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBufBytes];
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  // wave-uniform by construction; readfirstlane tells the compiler, so scalar buffer offsets that
+  // depend on it stay in SGPRs (otherwise every buffer load becomes a per-lane waterfall loop)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Unit order: each XCD takes a contiguous range of units, tile-major with the column chunks of a
+  // tile adjacent — the gathered activation tile is fetched once into that XCD's L2 and reused by
+  // its column chunks, and an expert's consecutive tiles reuse its weight slices from L2.
+  const int total = n_chunks * n_blocks;
+  const int per_xcd = (total + 7) >> 3;
+  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (u >= total) return;
+  const int blk = u / n_chunks, chunk = u - blk * n_chunks;
+  const int r0 = blk * kTileM;
+  if (r0 >= *p.num_post_pad) return;
+  const int e = p.block_expert[blk];
+  const int r1 = r0 + kTileM;
+  const int wchunk = chunk * kTileWaves + wave;  // this wave's 64-column chunk
+
+  TileRows<MT> tr;
+  tile_weights<WF, MT>(p, e, wchunk * 4, tr);
+  // Copy assignment: 8 consecutive lanes move one row's 128-byte K-step segment (a full cache
+  // line per 8 lanes); thread t handles rows 32q + t/8 (q = 0..3), 16-byte unit t % 8.
+  // Threads t < 128 also move row t's 16 scale bytes of the K-step's group.
+  const int cunit = tid & 7, crow0 = tid >> 3;
+  uint32_t coff[4], csoff = kOutOfRange;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = r0 + 32 * q + crow0;
+    bool ok = true;
+    int ar = r;
+    if (GATE_UP) {
+      const int sid = p.sorted_ids[r];
+      ok = sid < p.S;
+      ar = sid / p.k1;
+    }
+    coff[q] = ok ? (uint32_t)ar * (uint32_t)p.a_stride + 16u * cunit : kOutOfRange;
+  }
+  if (tid < kTileM) {
+    const int r = r0 + tid;
+    bool ok = true;
+    int ar = r;
+    if (GATE_UP) {
+      const int sid = p.sorted_ids[r];
+      ok = sid < p.S;
+      ar = sid / p.k1;
+    }
+    csoff = ok ? (uint32_t)ar * (uint32_t)p.a_srs : kOutOfRange;
+  }
+
+  v4f acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // P-deep register ring: the weight fragments, the activation bytes and scale bytes this thread
+  // copies into LDS for K-step ks + P are requested while step ks is multiplied; LDS is
+  // double-buffered (step ks + 1 is written while step ks is read).
+  Stage<WF, 1> bst[P];
+  v4i ca[P][4];
+  v4i cs[P];
+  auto load_copy = [&](int ks, int slot) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      ca[slot][q] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, coff[q], ks * KSTEP, 0);
+    if (tid < kTileM) cs[slot] = __builtin_amdgcn_raw_buffer_load_b128(tr.as, csoff, 16 * (ks >> 2), 0);
+  };
+  auto store_copy = [&](int slot, int buf) {
+    uint8_t* dst = lds[buf];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * q + crow0;
+      *(v4i*)(dst + row * kLdsPitch + lds_unit(row, cunit)) = ca[slot][q];
+    }
+    if (tid < kTileM) *(v4i*)(dst + kTileBytes + 16 * tid) = cs[slot];
+  };
+  auto load_all = [&](int ks, int slot) {
+    load_b<WF, 1, MT>(p, tr, ks, lane, bst[slot]);
+    load_copy(ks, slot);
+  };
+  auto compute = [&](int ks, int buf, const Stage<WF, 1>& b) {
+    const int sh = 8 * (ks & 3);
+    // rows n + 16 mt share (row & 7) = n & 7, so the swizzled units are loop-invariant
+    const uint8_t* base = lds[buf] + n * kLdsPitch;
+    const uint8_t* sbase = lds[buf] + kTileBytes + 16 * n + 4 * g;
+    const int u0 = lds_unit(n, g), u1 = lds_unit(n, 4 + g);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v8i a8;
+      a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
+      a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
+      const uint32_t sa = *(const uint32_t*)(sbase + 256 * mt);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        v8i b8;
+        b8.lo = b.b[f][0];
+        b8.hi = (WF == WF_FP8) ? b.b[f][1] : v4i{0, 0, 0, 0};
+        acc[mt][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a8, b8, acc[mt][f], 0, WF == WF_FP4 ? 4 : 0, 0, (int)(sa >> sh), 0,
+            (int)(b.sb[f] >> sh));
+      }
+    }
+  };
+
+  if constexpr (P == 1) {
+    // single-step ring: next step's loads go out before this step's multiply; separate weight
+    // registers for the current and the next step
+    Stage<WF, 1> bnx;
+    load_all(0, 0);
+    store_copy(0, 0);
+    __syncthreads();
+    for (int ks = 0; ks < p.NKS; ++ks) {
+      const bool more = ks + 1 < p.NKS;
+      if (more) {
+        load_b<WF, 1, MT>(p, tr, ks + 1, lane, bnx);
+        load_copy(ks + 1, 0);
+      }
+      compute(ks, ks & 1, bst[0]);
+      if (more) store_copy(0, (ks + 1) & 1);
+      __syncthreads();
+      if (more) bst[0] = bnx;
+    }
+  } else {
+    // P divides NKS (host-checked), so every load in the steady-state loop is in range
+#pragma unroll
+    for (int s = 0; s < P; ++s) load_all(s, s);
+    store_copy(0, 0);
+    __syncthreads();
+    int k0 = 0;
+    for (; k0 + P < p.NKS; k0 += P) {
+#pragma unroll
+      for (int s = 0; s < P; ++s) {
+        const int ks = k0 + s;
+        compute(ks, ks & 1, bst[s]);
+        store_copy((s + 1) % P, (ks + 1) & 1);  // step ks + 1 (ks + 1 < NKS here)
+        load_all(ks + P, s);
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < P; ++s) {  // last group: no further loads
+      const int ks = k0 + s;
+      compute(ks, ks & 1, bst[s]);
+      if (s + 1 < P) store_copy(s + 1, (ks + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, r0, r1, wchunk, n, g);
+  else epilogue_down<MT>(p, acc, r0, r1, wchunk, n, g);
+}
+
 template <int WF, int MT, bool GATE_UP>
 __global__ __launch_bounds__(64) void k_gemm_direct(GemmParams p) {
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
@@ -356,7 +535,19 @@ template <int WF, bool GATE_UP>
 hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t st) {
   const int n_chunks = GATE_UP ? p.I / 32 : p.H / 64;
   if (large) {
-    hipLaunchKernelGGL((k_gemm_direct<WF, 4, GATE_UP>), dim3(n_chunks, n_blocks), dim3(64), 0, st, p);
+    const int n_tile_chunks = n_chunks / kTileWaves;
+    if (WF != WF_BF16 && p.block_m == kTileM && n_tile_chunks * kTileWaves == n_chunks) {
+      const int total = n_tile_chunks * n_blocks;
+      const dim3 grid(((total + 7) / 8) * 8), block(256);
+      constexpr int W = WF == WF_BF16 ? WF_FP8 : WF;
+      // ring depth: 2 K-steps when it divides the step count (3 would spill), else 1
+      if (p.NKS % 2 == 0)
+        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, 2>), grid, block, 0, st, p, n_tile_chunks, n_blocks);
+      else
+        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, 1>), grid, block, 0, st, p, n_tile_chunks, n_blocks);
+    } else {
+      hipLaunchKernelGGL((k_gemm_direct<WF, 4, GATE_UP>), dim3(n_chunks, n_blocks), dim3(64), 0, st, p);
+    }
     return hipGetLastError();
   }
   switch (stream_depth(WF, p.NKS)) {

@@ -98,13 +98,14 @@ struct GemmParams {
   const float* topk_w;
   float* out32;              // slot rows [S, H] or token rows [T, H]
   int H;
-  int combine;               // 1 slots, 2 atomic
+  int combine;               // 1 fp32 slot rows, 2 fp32 atomics, 3 bf16 slot rows
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 
 // finalize.hip
-hipError_t launch_finalize(const float* out32, int T, int H, int k1, bool slots, uint16_t* y,
+// combine: 1 fp32 slot rows, 2 fp32 token rows, 3 bf16 slot rows.
+hipError_t launch_finalize(const void* out, int T, int H, int k1, int combine, uint16_t* y,
                            hipStream_t st);
 
 }  // namespace mxmoe
