@@ -334,7 +334,6 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
-    gu.NKG = (gu.NKS + 3) / 4;
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);
@@ -350,7 +349,6 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.ws = (const uint8_t*)s2_p;
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
-    dn.NKG = (dn.NKS + 3) / 4;
     e = launch_down(P.wf, P.large, dn, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(3);

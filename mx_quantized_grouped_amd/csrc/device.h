@@ -7,6 +7,7 @@ namespace mxmoe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -74,13 +75,8 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, int se) {
 }
 
 // ---------------------------------------------------------------------------- layouts
-// Kernel-native scale layout of an activation / intermediate row: the scale of K-block kb lives
-// at byte 16*(ks/4) + 4*(kb%4) + ks%4, ks = kb/4 the MFMA K-step. One dword load at
-// 16*kg + 4*g then gives lane group g the scales of four consecutive K-steps (byte ks%4).
-__device__ __host__ __forceinline__ int act_scale_byte(int kb) {
-  int ks = kb >> 2;
-  return ((ks >> 2) << 4) + ((kb & 3) << 2) + (ks & 3);
-}
+// Scales of an activation / intermediate row are stored in K-block order, one byte per 32 elements,
+// in rows padded to a multiple of 16 bytes: the four K-blocks of one 128-K MFMA step are one dword.
 __device__ __host__ __forceinline__ int round_up(int a, int b) { return (a + b - 1) / b * b; }
 
 }  // namespace mxmoe

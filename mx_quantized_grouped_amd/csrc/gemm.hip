@@ -22,6 +22,7 @@
 // more than one tile reads its weights from HBM once, the grouped-MoE program ordering of the
 // MiniMax-M3 page's local-shapes passage.
 #include <cstdlib>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -40,8 +41,8 @@ template <int WF, int MT>
 struct Stage {
   v4i b[4][WF == WF_BF16 ? 4 : 2];
   v4i a[MT][WF == WF_BF16 ? 4 : 2];
-  uint32_t sb[4];
-  uint32_t sa[MT];
+  uint32_t sb;      // byte f: scale of fragment f for this lane's (row, K-block)
+  uint32_t sa[MT];  // byte g: scale of K-block 4 ks + g of the lane's row
 };
 
 // Buffer descriptor of a raw byte range (gfx9 raw-buffer format word); loads past num_bytes
@@ -69,7 +70,7 @@ __device__ __forceinline__ void tile_weights(const GemmParams& p, int e, int nt0
   const size_t wbytes = (size_t)p.NT * p.NKS * FB;
   tr.w = raw_rsrc(p.w + (size_t)e * wbytes, (uint32_t)wbytes);
   if (WF != WF_BF16) {
-    const size_t sbytes = (size_t)p.NT * p.NKG * 256;
+    const size_t sbytes = (size_t)(p.NT / 4) * p.NKS * 256;
     tr.ws = raw_rsrc(p.ws + (size_t)e * sbytes, (uint32_t)sbytes);
     tr.as = raw_rsrc(p.as, p.as_bytes);
   }
@@ -97,7 +98,7 @@ __device__ __forceinline__ void tile_act_rows(const GemmParams& p, int m0, int r
       ar = r;
     }
     tr.aoff[mt] = ok ? (uint32_t)ar * (uint32_t)p.a_stride + 16u * g : kOutOfRange;
-    tr.asoff[mt] = ok ? (uint32_t)ar * (uint32_t)p.a_srs + 4u * g : kOutOfRange;
+    tr.asoff[mt] = ok ? (uint32_t)ar * (uint32_t)p.a_srs : kOutOfRange;
   }
 }
 
@@ -119,10 +120,9 @@ __device__ __forceinline__ void load_b(const GemmParams& p, const TileRows<MTR>&
       for (int q = 0; q < 4; ++q)
         s.b[f][q] = __builtin_amdgcn_raw_buffer_load_b128(tr.w, vo + 1024u * q, soff, 0);
     }
-    if (WF != WF_BF16)
-      s.sb[f] = __builtin_amdgcn_raw_buffer_load_b32(tr.ws, 4u * lane,
-                                                     ((tr.nt0 + f) * p.NKG + (ks >> 2)) * 256, 0);
   }
+  if (WF != WF_BF16)
+    s.sb = __builtin_amdgcn_raw_buffer_load_b32(tr.ws, 4u * lane, ((tr.nt0 >> 2) * p.NKS + ks) * 256, 0);
 }
 
 template <int WF, int MT>
@@ -132,7 +132,7 @@ __device__ __forceinline__ void load_a(const TileRows<MT>& tr, int ks, Stage<WF,
     if (WF != WF_BF16) {
       s.a[mt][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, tr.aoff[mt], ks * KSTEP, 0);
       s.a[mt][1] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, tr.aoff[mt] + 64u, ks * KSTEP, 0);
-      s.sa[mt] = __builtin_amdgcn_raw_buffer_load_b32(tr.as, tr.asoff[mt], 16 * (ks >> 2), 0);
+      s.sa[mt] = __builtin_amdgcn_raw_buffer_load_b32(tr.as, tr.asoff[mt], 4 * ks, 0);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -149,34 +149,59 @@ __device__ __forceinline__ void load_stage(const GemmParams& p, const TileRows<M
   load_a<WF, MT>(tr, ks, s);
 }
 
+// The four block-scaled MFMAs of one A fragment against the wave's 4 weight fragments; the scale
+// operand of fragment F is byte F of sb (selected by the instruction's op_sel).
+template <int WF, int F = 0>
+__device__ __forceinline__ void mma_frags(const v8i& a8, int sa, const v4i (&b)[4][2], int sb,
+                                          v4f (&acc)[4]) {
+  if constexpr (F < 4) {
+    v8i b8;
+    b8.lo = b[F][0];
+    b8.hi = (WF == WF_FP8) ? b[F][1] : v4i{0, 0, 0, 0};
+    acc[F] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[F], 0,
+                                                              WF == WF_FP4 ? 4 : 0, 0, sa, F, sb);
+    mma_frags<WF, F + 1>(a8, sa, b, sb, acc);
+  }
+}
+
+// ash = 8 * (lane / 16): the lane's K-block byte within the A scale dword.
 template <int WF, int MT>
-__device__ __forceinline__ void mma_stage(const Stage<WF, MT>& s, int ks, v4f (&acc)[MT][4]) {
-  const int sh = 8 * (ks & 3);
+__device__ __forceinline__ void mma_stage(const Stage<WF, MT>& s, int ash, v4f (&acc)[MT][4]) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    if constexpr (WF != WF_BF16) {
+      v8i a8;
+      a8.lo = s.a[mt][0];
+      a8.hi = s.a[mt][1];
+      mma_frags<WF>(a8, (int)(s.sa[mt] >> ash), s.b, (int)s.sb, acc[mt]);
+    } else {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (WF != WF_BF16) {
-        v8i a8, b8;
-        a8.lo = s.a[mt][0];
-        a8.hi = s.a[mt][1];
-        b8.lo = s.b[f][0];
-        b8.hi = (WF == WF_FP8) ? s.b[f][1] : v4i{0, 0, 0, 0};
-        acc[mt][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a8, b8, acc[mt][f], 0, WF == WF_FP4 ? 4 : 0, 0, (int)(s.sa[mt] >> sh), 0,
-            (int)(s.sb[f] >> sh));
-      } else {
+      for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           acc[mt][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(v8bf, s.a[mt][q]), __builtin_bit_cast(v8bf, s.b[f][q]),
               acc[mt][f], 0, 0, 0);
-      }
     }
   }
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (about 1 ulp); exp overflow for very negative g gives
+// g * rcp(inf) = -0, the limit.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), in every lane of the row: the
+// row of an MFMA result fragment, i.e. one 16-column slice of four output rows.
+__device__ __forceinline__ float row16_max(float v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
 
 // acc[mt][f][i] is C[row 4g+i of tile mt][column n of fragment f]. Fragments 0/1 are gate/up of
 // intermediate columns chunk*32 + 0..15, fragments 2/3 of chunk*32 + 16..31.
@@ -192,15 +217,13 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
       float a0 = silu(acc[mt][0][i]) * acc[mt][1][i];
       float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
       if (WF != WF_BF16) {
-        float m = fmaxf(fabsf(a0), fabsf(a1));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
         int se = mx_shared_exp<8>(m);
         if (rr < r1) {
           uint8_t* hr = p.h + (size_t)rr * p.h_stride + ic0;
           hr[n] = (uint8_t)e4m3_code(a0, se);
           hr[16 + n] = (uint8_t)e4m3_code(a1, se);
-          if (n == 0) p.hs[(size_t)rr * p.h_srs + act_scale_byte(chunk)] = (uint8_t)(se + 127);
+          if (n == 0) p.hs[(size_t)rr * p.h_srs + chunk] = (uint8_t)(se + 127);
         }
       } else if (rr < r1) {
         uint16_t* hr = (uint16_t*)(p.h + (size_t)rr * p.h_stride) + ic0;
@@ -219,7 +242,7 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
           for (int c = p.I + n; c < p.Ip; c += 16) p.h[(size_t)rr * p.h_stride + c] = 0;
           if (n == 0)
             for (int kb = p.I / 32; kb < p.Ip / 32; ++kb)
-              p.hs[(size_t)rr * p.h_srs + act_scale_byte(kb)] = 127;
+              p.hs[(size_t)rr * p.h_srs + kb] = 127;
         } else {
           uint16_t* hr = (uint16_t*)(p.h + (size_t)rr * p.h_stride);
           for (int c = p.I + n; c < p.Ip; c += 16) hr[c] = 0;
@@ -296,12 +319,12 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     for (; k0 + D < p.NKS; k0 += D) {
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        mma_stage<WF, MT>(buf[s], k0 + s, acc);
+        mma_stage<WF, MT>(buf[s], 8 * g, acc);
         load_stage<WF, MT>(p, tr, k0 + s + D, lane, buf[s]);
       }
     }
 #pragma unroll
-    for (int s = 0; s < D; ++s) mma_stage<WF, MT>(buf[s], k0 + s, acc);
+    for (int s = 0; s < D; ++s) mma_stage<WF, MT>(buf[s], 8 * g, acc);
     if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
     else epilogue_down<MT>(p, acc, m0, r1, chunk, n, g);
   }
@@ -309,28 +332,141 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
 
 // ------------------------------------------------------------------------------ large-M
 // Prefill launcher: a workgroup of 4 waves computes a 128-row x 256-column tile (rows of one expert
-// from the sorted layout). The gathered activation tile of each 128-K step is staged through LDS
-// (double-buffered) and shared by the 4 waves; each wave streams its own 4 weight fragments (64
-// columns) into registers, one K-step ahead. Per K-step a wave issues 8 x 4 block-scaled MFMAs.
-// LDS rows are 128 bytes with the eight 16-byte column units of row r stored at unit c ^ (r & 7):
-// the 16 rows an MFMA operand read touches then spread over all banks (measured on gfx950: ~198
-// B/clk/CU for this read pattern, against ~119 with 16-byte row padding).
+// from the sorted layout); each wave owns 64 columns (4 weight fragments) for all 128 rows, i.e.
+// 8 x 4 block-scaled MFMAs per 128-K step.
+//
+// Every operand of a K-step travels global -> LDS by the buffer unit's direct LDS loads (no
+// staging registers): the gathered 128 x 128-byte activation tile, the tile's activation scales,
+// each wave's 4 weight fragments and their scale dwords. LDS holds three stages, so the loads of
+// step ks + 2 are in flight while step ks is multiplied. A direct LDS load writes lane i's bytes
+// at (base + size * i), so the global address each lane requests decides the LDS layout:
+//   * activation rows are 128 bytes with the eight 16-byte units of row r stored at unit
+//     c ^ (r & 7) — the 16 rows an MFMA operand read touches then spread over all banks (measured
+//     on gfx950: ~198 B/clk/CU for this read pattern, against ~119 with 16-byte row padding);
+//   * weight fragments keep their prepacked [half][lane][16 B] order (contiguous reads).
+// Stage completion is a wait on the wave's own load counter followed by a workgroup barrier; it is
+// written as one asm statement because the compiler's barrier would first wait for all
+// outstanding loads, including the next stage's.
 constexpr int kTileM = 128;
 constexpr int kTileWaves = 4;
 constexpr int kLdsPitch = KSTEP;
-__device__ __forceinline__ int lds_unit(int row, int c) { return (c ^ (row & 7)) << 4; }
 
-template <int WF, bool GATE_UP, int P>
-__global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
+template <int WF>
+struct TileLds {
+  static constexpr int a = 0;                          // 128 rows x 128 B
+  static constexpr int as = kTileM * kLdsPitch;        // per wave 256 B of A scale dwords
+  static constexpr int bs = as + kTileWaves * 256;     // per wave 64 B scale dwords
+  static constexpr int b = bs + kTileWaves * 256;      // per wave 4 fragments
+  static constexpr int bytes = b + kTileWaves * 4 * Frag<WF>::bytes;
+  static constexpr int stages = 3;
+  // direct LDS loads per wave and K-step: 4 activation, 1 A scale, 1 B scale, the fragments
+  static constexpr int loads = 4 + 1 + 1 + 4 * Frag<WF>::bytes / 1024;
+};
+
+// Raw buffer descriptor words (same format as raw_rsrc) for the asm loads below.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_bytes) {
+  const uint64_t a = (uint64_t)base;
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)num_bytes, 0x00020000};
+}
+
+// Direct global -> LDS loads: lane i's 16 (or 4) bytes land at LDS byte lds + 16 i (or 4 i).
+// They are issued from asm so that the compiler does not add its own (all-outstanding) waits
+// before every LDS read; completion is tracked explicitly with wait_loads_barrier.
+__device__ __forceinline__ void lds_load16(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+__device__ __forceinline__ void lds_load4(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and its LDS reads are
+// done, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// gate_up epilogue of a 128-row x 256-column tile: the workgroup's 4 waves hold the gate/up
+// pairs of 4 consecutive MX blocks (128 intermediate columns) of every row. SwiGLU and the MXFP8
+// requantisation run in registers; codes and scale bytes are staged in LDS, then each row's 128
+// code bytes go out as 16-byte stores (8 lanes per row) and its 4 scale bytes as one dword (the
+// scale layout is in K-block order). Rows of padding slots are written too (their codes are zero
+// since their activation rows read as zero), so the down pass can read every row of a tile.
+template <int WF>
+__device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const v4f (&acc)[8][4],
+                                                      int r0, int chunk, int wave, int n, int g,
+                                                      int tid, uint8_t* lds) {
+  constexpr int kPitch = 128 + 16;           // code row pitch in LDS
+  uint8_t* codes = lds;                      // [128][kPitch]
+  uint32_t* scales = (uint32_t*)(lds + kTileM * kPitch);  // [128] dwords, byte = wave
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * mt + 4 * g + i;
+      const float a0 = silu(acc[mt][0][i]) * acc[mt][1][i];
+      const float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
+      const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
+      const int se = mx_shared_exp<8>(m);
+      codes[row * kPitch + 32 * wave + n] = (uint8_t)e4m3_code(a0, se);
+      codes[row * kPitch + 32 * wave + 16 + n] = (uint8_t)e4m3_code(a1, se);
+      if (n == 0) ((uint8_t*)scales)[4 * row + wave] = (uint8_t)(se + 127);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j, row = c >> 3, unit = c & 7;
+    *(v4i*)(p.h + (size_t)(r0 + row) * p.h_stride + 128 * chunk + 16 * unit) =
+        *(const v4i*)(codes + row * kPitch + 16 * unit);
+  }
+  if (tid < kTileM)
+    *(uint32_t*)(p.hs + (size_t)(r0 + tid) * p.h_srs + 4 * chunk) = scales[tid];
+}
+
+// down epilogue with bf16 slot rows: the tile's 128 x 256 bf16 products w(row) * d(row) are staged
+// in LDS (row pitch 512 + 32 bytes, so the four rows one store instruction touches fall in
+// different banks), then each slot row's 512-byte segment goes out as 16-byte stores (32 lanes per
+// row); rows of padding slots are skipped.
+__device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4f (&acc)[8][4],
+                                                   int r0, int chunk, int wave, int n, int g,
+                                                   int tid, uint8_t* lds, const int* row_sid,
+                                                   const float* row_w) {
+  constexpr int kPitch = 512 + 32;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const v4f wt = *(const v4f*)(row_w + 16 * mt + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t* orow = (uint16_t*)(lds + (16 * mt + 4 * g + i) * kPitch) + 64 * wave + n;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) orow[16 * f] = (uint16_t)f32_to_bf16_bits(wt[i] * acc[mt][f][i]);
+    }
+  }
+  __syncthreads();
+  uint16_t* out16 = (uint16_t*)p.out32;
+#pragma unroll 4
+  for (int j = 0; j < 16; ++j) {
+    const int c = tid + 256 * j, row = c >> 5, unit = c & 31;
+    const int sid = row_sid[row];
+    if (sid < p.S)
+      *(v4i*)(out16 + (size_t)sid * p.H + 256 * chunk + 8 * unit) =
+          *(const v4i*)(lds + row * kPitch + 16 * unit);
+  }
+}
+
+template <int WF, bool GATE_UP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
+  using L = TileLds<WF>;
   constexpr int MT = kTileM / 16;
-  // per buffer: the 128 x 128-byte activation tile, then the tile's scale bytes for the K-step's
-  // group (16 bytes per row: the four lane-group dwords of the kernel-native scale layout)
-  constexpr int kTileBytes = kTileM * kLdsPitch;
-  constexpr int kBufBytes = kTileBytes + kTileM * 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBufBytes];
+  constexpr int FB = Frag<WF>::bytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::stages * L::bytes];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  // wave-uniform by construction; readfirstlane tells the compiler, so scalar buffer offsets that
-  // depend on it stay in SGPRs (otherwise every buffer load becomes a per-lane waterfall loop)
+  // wave-uniform by construction; readfirstlane tells the compiler, so the scalar offsets and LDS
+  // addresses of the loads below stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Unit order: each XCD takes a contiguous range of units, tile-major with the column chunks of a
   // tile adjacent — the gathered activation tile is fetched once into that XCD's L2 and reused by
@@ -345,37 +481,64 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p, int n_chunks, i
   const int e = p.block_expert[blk];
   const int r1 = r0 + kTileM;
   const int wchunk = chunk * kTileWaves + wave;  // this wave's 64-column chunk
+  const int nt0 = wchunk * 4;
+  // down: slot id and routing weight of each tile row, for the combine epilogue
+  __shared__ __attribute__((aligned(16))) int row_sid[kTileM];
+  __shared__ __attribute__((aligned(16))) float row_w[kTileM];
+  if (!GATE_UP && tid < kTileM) {
+    const int sid = p.sorted_ids[r0 + tid];
+    row_sid[tid] = sid;
+    row_w[tid] = sid < p.S ? p.topk_w[sid] : 0.f;
+  }
+  const size_t wbytes = (size_t)p.NT * p.NKS * FB;
+  const size_t sbytes = (size_t)(p.NT / 4) * p.NKS * 256;
+  const v4i rw = rsrc_words(p.w + (size_t)e * wbytes, (uint32_t)wbytes);
+  const v4i rws = rsrc_words(p.ws + (size_t)e * sbytes, (uint32_t)sbytes);
+  const v4i ra = rsrc_words(p.a, p.a_bytes);
+  const v4i ras = rsrc_words(p.as, p.as_bytes);
 
-  TileRows<MT> tr;
-  tile_weights<WF, MT>(p, e, wchunk * 4, tr);
-  // Copy assignment: 8 consecutive lanes move one row's 128-byte K-step segment (a full cache
-  // line per 8 lanes); thread t handles rows 32q + t/8 (q = 0..3), 16-byte unit t % 8.
-  // Threads t < 128 also move row t's 16 scale bytes of the K-step's group.
-  const int cunit = tid & 7, crow0 = tid >> 3;
-  uint32_t coff[4], csoff = kOutOfRange;
+  // Source row offsets. Activation load j of this wave fills tile rows 32 wave + 8 j + lane / 8;
+  // the lane fetches the unit that belongs at LDS unit lane % 8 of that row.
+  auto act_row = [&](int r, uint32_t stride) -> uint32_t {
+    if (GATE_UP) {
+      const int sid = p.sorted_ids[r];
+      return sid < p.S ? (uint32_t)(sid / p.k1) * stride : kOutOfRange;
+    }
+    return (uint32_t)r * stride;
+  };
+  uint32_t aoff[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = r0 + 32 * q + crow0;
-    bool ok = true;
-    int ar = r;
-    if (GATE_UP) {
-      const int sid = p.sorted_ids[r];
-      ok = sid < p.S;
-      ar = sid / p.k1;
+  for (int j = 0; j < 4; ++j)
+    aoff[j] = act_row(r0 + 32 * wave + 8 * j + (lane >> 3), (uint32_t)p.a_stride) +
+              16u * ((lane & 7) ^ (lane >> 3));
+  // A scale dwords: waves 0 and 1 fetch rows 64 wave + lane; waves 2 and 3 issue the same load
+  // out of range (zeros into their own unused slot), so every wave counts the same loads.
+  const uint32_t asoff = wave < 2 ? act_row(r0 + 64 * wave + lane, (uint32_t)p.a_srs) : kOutOfRange;
+  const int bs_base = (nt0 >> 2) * p.NKS * 256;
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  // Load q (0 .. L::loads - 1) of a K-step: 0-3 activation rows, 4 A scales, 5 B scales, then the
+  // weight fragments. oob = kOutOfRange turns it into an out-of-range load (it writes zeros and
+  // moves no data), so steps past the end still issue the same number of loads.
+  auto issue_one = [&](int q, uint32_t st, int ks, uint32_t oob) {
+    if (q < 4) {
+      lds_load16(ra, st + L::a + (32 * wave + 8 * q) * kLdsPitch, aoff[q] | oob, ks * KSTEP);
+    } else if (q == 4) {
+      lds_load4(ras, st + L::as + 256 * wave, asoff | oob, 4 * ks);
+    } else if (q == 5) {
+      lds_load4(rws, st + L::bs + 256 * wave, (4u * lane) | oob, bs_base + ks * 256);
+    } else {
+      constexpr int H = FB / 1024;
+      const int f = (q - 6) / H, h = (q - 6) % H;
+      lds_load16(rw, st + L::b + (4 * wave + f) * FB + 1024 * h, (16u * lane + 1024u * h) | oob,
+                 ((nt0 + f) * p.NKS + ks) * FB);
     }
-    coff[q] = ok ? (uint32_t)ar * (uint32_t)p.a_stride + 16u * cunit : kOutOfRange;
-  }
-  if (tid < kTileM) {
-    const int r = r0 + tid;
-    bool ok = true;
-    int ar = r;
-    if (GATE_UP) {
-      const int sid = p.sorted_ids[r];
-      ok = sid < p.S;
-      ar = sid / p.k1;
-    }
-    csoff = ok ? (uint32_t)ar * (uint32_t)p.a_srs : kOutOfRange;
-  }
+  };
+  auto issue = [&](int stage, int ks, uint32_t oob) {
+    const uint32_t st = lds0 + stage * L::bytes;
+#pragma unroll
+    for (int q = 0; q < L::loads; ++q) issue_one(q, st, ks, oob);
+  };
 
   v4f acc[MT][4];
 #pragma unroll
@@ -383,101 +546,67 @@ __global__ __launch_bounds__(256) void k_gemm_tile(GemmParams p, int n_chunks, i
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // P-deep register ring: the weight fragments, the activation bytes and scale bytes this thread
-  // copies into LDS for K-step ks + P are requested while step ks is multiplied; LDS is
-  // double-buffered (step ks + 1 is written while step ks is read).
-  Stage<WF, 1> bst[P];
-  v4i ca[P][4];
-  v4i cs[P];
-  auto load_copy = [&](int ks, int slot) {
+  // rows n + 16 mt share (row & 7) = n & 7, so the swizzled units are loop-invariant
+  const int u0 = (g ^ (n & 7)) << 4, u1 = ((4 + g) ^ (n & 7)) << 4;
+  // Multiply the stage's tile while issuing the next-but-one step's loads, four of them before
+  // every other 16-row group, so that the load issue overlaps the matrix cores instead of
+  // preceding them (measured on the 8K-token prefill: 314 us for gate_up against 347 us with all
+  // loads issued at the start of the step).
+  auto compute_issue = [&](int stage, int nstage, int ks2, uint32_t oob) {
+    const uint8_t* st = lds + stage * L::bytes;
+    const uint32_t nst = lds0 + nstage * L::bytes;
+    v4i b[4][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      ca[slot][q] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, coff[q], ks * KSTEP, 0);
-    if (tid < kTileM) cs[slot] = __builtin_amdgcn_raw_buffer_load_b128(tr.as, csoff, 16 * (ks >> 2), 0);
-  };
-  auto store_copy = [&](int slot, int buf) {
-    uint8_t* dst = lds[buf];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 32 * q + crow0;
-      *(v4i*)(dst + row * kLdsPitch + lds_unit(row, cunit)) = ca[slot][q];
+    for (int f = 0; f < 4; ++f) {
+      b[f][0] = *(const v4i*)(st + L::b + (4 * wave + f) * FB + 16 * lane);
+      b[f][1] = WF == WF_FP8 ? *(const v4i*)(st + L::b + (4 * wave + f) * FB + 1024 + 16 * lane)
+                             : v4i{0, 0, 0, 0};
     }
-    if (tid < kTileM) *(v4i*)(dst + kTileBytes + 16 * tid) = cs[slot];
-  };
-  auto load_all = [&](int ks, int slot) {
-    load_b<WF, 1, MT>(p, tr, ks, lane, bst[slot]);
-    load_copy(ks, slot);
-  };
-  auto compute = [&](int ks, int buf, const Stage<WF, 1>& b) {
-    const int sh = 8 * (ks & 3);
-    // rows n + 16 mt share (row & 7) = n & 7, so the swizzled units are loop-invariant
-    const uint8_t* base = lds[buf] + n * kLdsPitch;
-    const uint8_t* sbase = lds[buf] + kTileBytes + 16 * n + 4 * g;
-    const int u0 = lds_unit(n, g), u1 = lds_unit(n, 4 + g);
+    const int sb = *(const int*)(st + L::bs + 256 * wave + 4 * lane);
+    const uint8_t* base = st + L::a + n * kLdsPitch;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       v8i a8;
       a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
       a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
-      const uint32_t sa = *(const uint32_t*)(sbase + 256 * mt);
+      const uint32_t sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
+      if (mt % 2 == 0) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        v8i b8;
-        b8.lo = b.b[f][0];
-        b8.hi = (WF == WF_FP8) ? b.b[f][1] : v4i{0, 0, 0, 0};
-        acc[mt][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a8, b8, acc[mt][f], 0, WF == WF_FP4 ? 4 : 0, 0, (int)(sa >> sh), 0,
-            (int)(b.sb[f] >> sh));
+        for (int q = 2 * mt; q < 2 * mt + 4; ++q)
+          if (q < L::loads) issue_one(q, nst, ks2, oob);
       }
+      mma_frags<WF>(a8, (int)(sa >> (8 * g)), b, sb, acc[mt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  if constexpr (P == 1) {
-    // single-step ring: next step's loads go out before this step's multiply; separate weight
-    // registers for the current and the next step
-    Stage<WF, 1> bnx;
-    load_all(0, 0);
-    store_copy(0, 0);
-    __syncthreads();
-    for (int ks = 0; ks < p.NKS; ++ks) {
-      const bool more = ks + 1 < p.NKS;
-      if (more) {
-        load_b<WF, 1, MT>(p, tr, ks + 1, lane, bnx);
-        load_copy(ks + 1, 0);
-      }
-      compute(ks, ks & 1, bst[0]);
-      if (more) store_copy(0, (ks + 1) & 1);
-      __syncthreads();
-      if (more) bst[0] = bnx;
-    }
-  } else {
-    // P divides NKS (host-checked), so every load in the steady-state loop is in range
-#pragma unroll
-    for (int s = 0; s < P; ++s) load_all(s, s);
-    store_copy(0, 0);
-    __syncthreads();
-    int k0 = 0;
-    for (; k0 + P < p.NKS; k0 += P) {
-#pragma unroll
-      for (int s = 0; s < P; ++s) {
-        const int ks = k0 + s;
-        compute(ks, ks & 1, bst[s]);
-        store_copy((s + 1) % P, (ks + 1) & 1);  // step ks + 1 (ks + 1 < NKS here)
-        load_all(ks + P, s);
-        __syncthreads();
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < P; ++s) {  // last group: no further loads
-      const int ks = k0 + s;
-      compute(ks, ks & 1, bst[s]);
-      if (s + 1 < P) store_copy(s + 1, (ks + 1) & 1);
-      __syncthreads();
-    }
+  // Step ks reads stage ks % 3. The loads of step ks + 2 go out first, into the stage step ks - 1
+  // read (every wave has passed the barrier after it); the barrier at the end of the step makes
+  // step ks + 1's stage complete for all waves while step ks + 2's loads stay in flight. The body
+  // has no branch (steps past the end issue out-of-range loads), and a scheduling barrier keeps
+  // the MFMAs ahead of the wait.
+  const int nks = p.NKS;
+  issue(0, 0, 0u);
+  issue(1, 1, nks > 1 ? 0u : kOutOfRange);
+  wait_loads_barrier<L::loads>();
+  static_assert(L::loads <= 2 * MT, "loads must fit the 16-row groups");
+  int stage = 0;
+  for (int ks = 0; ks < nks; ++ks) {
+    compute_issue(stage, stage == 0 ? 2 : stage - 1, ks + 2, ks + 2 < nks ? 0u : kOutOfRange);
+    wait_loads_barrier<L::loads>();
+    stage = stage == 2 ? 0 : stage + 1;
   }
-
-  if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, r0, r1, wchunk, n, g);
-  else epilogue_down<MT>(p, acc, r0, r1, wchunk, n, g);
+  // the last steps' out-of-range loads still write zeros into LDS: drain them in every wave
+  wait_loads_barrier<0>();
+  // Every wave has passed the last barrier, so the stage buffers are free: the epilogues stage the
+  // output tile there and write whole rows with 16-byte stores (the per-lane MFMA layout holds one
+  // column of four rows, which stored directly means 1- or 2-byte scattered stores).
+  if constexpr (GATE_UP) {
+    epilogue_gate_up_tile<WF>(p, acc, r0, chunk, wave, n, g, tid, lds);
+  } else {
+    if (p.combine == 3) epilogue_down_tile(p, acc, r0, chunk, wave, n, g, tid, lds, row_sid, row_w);
+    else epilogue_down<MT>(p, acc, r0, r1, wchunk, n, g);
+  }
 }
 
 template <int WF, int MT, bool GATE_UP>
@@ -501,7 +630,7 @@ __global__ __launch_bounds__(64) void k_gemm_direct(GemmParams p) {
     load_stage<WF, MT>(p, tr, 0, lane, cur);
     for (int ks = 0; ks < p.NKS; ++ks) {
       if (ks + 1 < p.NKS) load_stage<WF, MT>(p, tr, ks + 1, lane, nxt);
-      mma_stage<WF, MT>(cur, ks, acc);
+      mma_stage<WF, MT>(cur, 8 * g, acc);
       if (ks + 1 < p.NKS) cur = nxt;
     }
     if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
@@ -540,11 +669,7 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
       const int total = n_tile_chunks * n_blocks;
       const dim3 grid(((total + 7) / 8) * 8), block(256);
       constexpr int W = WF == WF_BF16 ? WF_FP8 : WF;
-      // ring depth: 2 K-steps when it divides the step count (3 would spill), else 1
-      if (p.NKS % 2 == 0)
-        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, 2>), grid, block, 0, st, p, n_tile_chunks, n_blocks);
-      else
-        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, 1>), grid, block, 0, st, p, n_tile_chunks, n_blocks);
+      hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP>), grid, block, 0, st, p, n_tile_chunks, n_blocks);
     } else {
       hipLaunchKernelGGL((k_gemm_direct<WF, 4, GATE_UP>), dim3(n_chunks, n_blocks), dim3(64), 0, st, p);
     }

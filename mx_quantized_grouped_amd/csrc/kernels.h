@@ -82,7 +82,7 @@ struct GemmParams {
   uint32_t as_bytes;         // size of the A scale matrix
   const uint8_t* w;          // prepacked weights
   const uint8_t* ws;         // prepacked weight scales (MX)
-  int NT, NKS, NKG;          // per expert: 16-row N tiles, K-steps of 128, groups of 4 K-steps
+  int NT, NKS;               // per expert: 16-row N tiles, K-steps of 128
   const int32_t* sorted_ids;
   const int32_t* expert_off;
   const int32_t* touched;

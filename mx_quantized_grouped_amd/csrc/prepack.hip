@@ -14,9 +14,10 @@
 // Fragments of an expert are ordered [16-row tile nt][K-step ks]. For W13 the tiles alternate gate
 // and up: tile 2p holds gate rows 16p..16p+15 and tile 2p+1 up rows I+16p..I+16p+15, so one wave
 // holds matching gate and up columns for the SwiGLU epilogue.
-// Scales: per (expert, tile nt, group of four K-steps kg) 64 dwords; lane l = n + 16g holds in byte j
-// the scale of row n, K-block 4*(4kg + j) + g (the operand order of the MFMA scale register, byte j
-// selected for K-step 4kg + j). K is zero-padded to a multiple of 128 (scale byte 127 there).
+// Scales: per (expert, group of four tiles q, K-step ks) 64 dwords; byte f of lane l = n + 16g is
+// the scale of row n of tile 4q + f for K-block 4ks + g. One dword load per lane and K-step serves
+// the four fragments a wave multiplies (the MFMA's scale operand selects byte f). K is zero-padded
+// to a multiple of 128 (scale byte 127 there). The tile count of an expert is a multiple of 4.
 #include "device.h"
 #include "kernels.h"
 
@@ -74,24 +75,23 @@ __global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t* src, uint8
 // One thread per prepacked scale dword.
 __global__ __launch_bounds__(256) void k_prepack_scales(const uint8_t* src, uint32_t* dst, int E1,
                                                         int N, int K, bool w13, int I) {
-  const int NT = N / 16, NKS = (K + KSTEP - 1) / KSTEP, NKG = (NKS + 3) / 4, KB = K / 32;
+  const int NQ = N / 64, NKS = (K + KSTEP - 1) / KSTEP, KB = K / 32;
   size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  size_t total = (size_t)E1 * NT * NKG * 64;
+  size_t total = (size_t)E1 * NQ * NKS * 64;
   if (idx >= total) return;
   int l = (int)(idx & 63);
   size_t r = idx >> 6;
-  int kg = (int)(r % NKG);
-  size_t en = r / NKG;
-  int nt = (int)(en % NT);
-  size_t e = en / NT;
-  int row = src_row(nt, l & 15, w13, I), g = l >> 4;
-  const uint8_t* s = src + ((size_t)e * N + row) * KB;
+  int ks = (int)(r % NKS);
+  size_t eq = r / NKS;
+  int q = (int)(eq % NQ);
+  size_t e = eq / NQ;
+  const int kb = 4 * ks + (l >> 4);
   uint32_t v = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int kb = 4 * (4 * kg + j) + g;
-    uint32_t b = kb < KB ? s[kb] : 127u;
-    v |= b << (8 * j);
+  for (int f = 0; f < 4; ++f) {
+    int row = src_row(4 * q + f, l & 15, w13, I);
+    uint32_t b = kb < KB ? src[((size_t)e * N + row) * KB + kb] : 127u;
+    v |= b << (8 * f);
   }
   dst[idx] = v;
 }
@@ -106,8 +106,8 @@ size_t prepack_code_bytes(const PrepackDims& d) {
 
 size_t prepack_scale_bytes(const PrepackDims& d) {
   if (d.wf == WF_BF16) return 0;
-  size_t NKS = (d.K + KSTEP - 1) / KSTEP, NKG = (NKS + 3) / 4;
-  return (size_t)d.E1 * (d.N / 16) * NKG * 256;
+  size_t NKS = (d.K + KSTEP - 1) / KSTEP;
+  return (size_t)d.E1 * (d.N / 64) * NKS * 256;
 }
 
 hipError_t launch_prepack(const PrepackDims& d, const void* codes, const uint8_t* scales,

@@ -55,8 +55,8 @@ __device__ __forceinline__ void encode_fp4_32(const float* v, int se, uint32_t* 
   }
 }
 
-// Activation block (t, kb) of bf16 x [T, H] -> E4M3 codes in xq [T, H] and the kernel-native scale
-// byte in xs [T, srs]; optionally clears the matching 32 floats of zero_out [T, H].
+// Activation block (t, kb) of bf16 x [T, H] -> E4M3 codes in xq [T, H] and the scale byte in
+// xs [T, srs] (K-block order); optionally clears the matching 32 floats of zero_out [T, H].
 __device__ __forceinline__ void quant_act_block(const uint16_t* x, size_t t, int kb, int H,
                                                 uint8_t* xq, uint8_t* xs, int srs,
                                                 float* zero_out) {
@@ -64,7 +64,7 @@ __device__ __forceinline__ void quant_act_block(const uint16_t* x, size_t t, int
   float v[32];
   load32<false>(x, off, v);
   int se = mx_shared_exp<8>(amax32(v));
-  xs[t * srs + act_scale_byte(kb)] = (uint8_t)(se + 127);
+  xs[t * srs + kb] = (uint8_t)(se + 127);
   uint32_t o[8];
   encode_fp8_32(v, se, o);
   v4i* p = (v4i*)(xq + off);

@@ -102,8 +102,8 @@ def test_shape_validation_and_sizes(L):
     assert B.mxmoe_prepacked_bytes(ok, 0) == E1 * 2 * I * H
     assert B.mxmoe_prepacked_bytes(ok, 1) == E1 * 2 * I * H // 32
     assert B.mxmoe_prepacked_bytes(ok, 2) == E1 * H * I
-    # scale dwords cover groups of four 128-K steps: I = 384 is 3 steps -> one (padded) group
-    assert B.mxmoe_prepacked_bytes(ok, 3) == E1 * (H // 16) * 1 * 256
+    # one scale dword per lane, 128-K step and group of four 16-row tiles: I = 384 is 3 steps
+    assert B.mxmoe_prepacked_bytes(ok, 3) == E1 * (H // 64) * 3 * 256
     f4 = B.Shape.of(128, 3072, 128, 8, 768, "mxfp4")
     assert B.mxmoe_prepacked_bytes(f4, 0) == E1 * 2 * 768 * 3072 // 2
     bf = B.Shape.of(16, 256, 8, 2, 128, "bf16")
