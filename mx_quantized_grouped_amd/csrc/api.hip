@@ -32,6 +32,10 @@ size_t cap_of(int S, int E1, int bm) {
   return (cap + bm - 1) / bm * bm;
 }
 
+// Largest batch whose final rounding runs inside the down pass: one wave per 64-column chunk
+// converts all T rows of its chunk, so the tail grows with T.
+constexpr int kFuseFinalMaxT = 256;
+
 bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 int check_route_args(int T, int E, int top_k) {
@@ -57,14 +61,15 @@ int check_shape(const mxmoe_shape* s) {
 
 enum Seg {
   SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF, SEG_TOUCHED, SEG_ALIGN,
-  SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, NSEG
+  SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, SEG_DONE, NSEG
 };
 
 struct Plan {
   int T, H, E, k, I, k1, S, E1;
   int wf;
   bool mx, large;
-  int combine;  // 1 slots, 2 atomic
+  int combine;  // 1 slots, 2 atomic, 3 bf16 slots
+  bool fuse_final;  // final bf16 rounding inside the down pass (small M, atomic combine)
   int bm, cap, Ip, srs_H, srs_I;
   size_t off[NSEG + 1];
 };
@@ -85,8 +90,12 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.large = o.launcher == MXMOE_LAUNCH_LARGE_M ||
             (o.launcher == MXMOE_LAUNCH_AUTO && p.S >= 16 * p.E1);
   // Large batches write bf16 slot rows (fp32 atomics run at about one value per L2 channel per
-  // cycle, far below what the prefill combine needs); small batches keep fp32 slot rows.
+  // cycle, far below what the prefill combine needs); small batches write fp32 slot rows. The
+  // atomic combine at small M rounds to bf16 inside the down pass (no final launch), but waiting
+  // for the atomics costs more than that launch at decode sizes (measured: 32 tokens, hidden
+  // 3072: down 52 us against 36 us plus a 3 us final pass).
   p.combine = o.combine ? o.combine : (p.large ? MXMOE_COMBINE_SLOTS_BF16 : MXMOE_COMBINE_SLOTS);
+  p.fuse_final = !p.large && p.combine == MXMOE_COMBINE_ATOMIC && p.T <= kFuseFinalMaxT;
   p.bm = o.block_m ? o.block_m : (p.large ? (p.mx ? 128 : 64) : 16);
   p.cap = (int)cap_of(p.S, p.E1, p.bm);
   p.Ip = round_up(p.I, KSTEP);
@@ -105,6 +114,7 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   sz[SEG_XS] = p.mx ? (size_t)p.T * p.srs_H : 0;
   sz[SEG_H] = (size_t)p.cap * p.Ip * (p.mx ? 1 : 2);
   sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
+  sz[SEG_DONE] = p.fuse_final ? (size_t)(p.H / 64) * 4 : 0;
   sz[SEG_OUT] = p.combine == MXMOE_COMBINE_ATOMIC ? (size_t)p.T * p.H * 4
                                                   : (size_t)p.S * p.H * (p.combine == MXMOE_COMBINE_SLOTS ? 4 : 2);
   size_t at = 0;
@@ -271,6 +281,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   uint8_t* h = (uint8_t*)(ws + P.off[SEG_H]);
   uint8_t* hs = (uint8_t*)(ws + P.off[SEG_HS]);
   float* out32 = (float*)(ws + P.off[SEG_OUT]);
+  int32_t* done = (int32_t*)(ws + P.off[SEG_DONE]);
   const bool slots = P.combine != MXMOE_COMBINE_ATOMIC;
 
   if (getenv("MXMOE_TRACE"))
@@ -299,6 +310,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   pa.xs = xs;
   pa.srs = P.srs_H;
   pa.zero_out = slots ? nullptr : out32;
+  pa.zero_cnt = P.fuse_final ? done : nullptr;
+  pa.n_cnt = P.fuse_final ? P.H / 64 : 0;
   if (e == hipSuccess) e = launch_prologue(pa, s->logits_dtype == MXMOE_F32, aws, st);
   const int n_blocks = P.cap / P.bm;
   GemmParams g{};
@@ -321,6 +334,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.topk_w = tw;
   g.out32 = out32;
   g.combine = P.combine;
+  g.T = P.T;
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
@@ -349,10 +363,15 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.ws = (const uint8_t*)s2_p;
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
+    if (P.fuse_final) {
+      dn.y = (uint16_t*)y;
+      dn.chunk_done = done;
+    }
     e = launch_down(P.wf, P.large, dn, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess) e = launch_finalize(out32, P.T, P.H, P.k1, P.combine, (uint16_t*)y, st);
+  if (e == hipSuccess && !P.fuse_final)
+    e = launch_finalize(out32, P.T, P.H, P.k1, P.combine, (uint16_t*)y, st);
   if (e == hipSuccess) e = mark(4);
   return hip_status(e);
 }

@@ -108,7 +108,7 @@ __device__ __forceinline__ void load_b(const GemmParams& p, const TileRows<MTR>&
   constexpr int FB = Frag<WF>::bytes;
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    const int soff = ((tr.nt0 + f) * p.NKS + ks) * FB;
+    const int soff = (((tr.nt0 >> 2) * p.NKS + ks) * 4 + f) * FB;
     const uint32_t vo = 16u * lane;
     if (WF == WF_FP8) {
       s.b[f][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.w, vo, soff, 0);
@@ -283,9 +283,64 @@ __device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&a
   }
 }
 
+// Down epilogue of the small-M launcher (one 16-row tile, rows 4g + i of the lane): slot id and
+// routing weight of each row were loaded when the wave started.
+__device__ __forceinline__ void epilogue_down_rows(const GemmParams& p, const v4f (&acc)[4],
+                                                   const int (&rsid)[4], const float (&rw)[4],
+                                                   int chunk, int n) {
+  const int c0 = 64 * chunk + n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sid = rsid[i];
+    if (sid >= p.S) continue;
+    if (p.combine == 3) {
+      uint16_t* orow = (uint16_t*)p.out32 + (size_t)sid * p.H;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) orow[c0 + 16 * f] = (uint16_t)f32_to_bf16_bits(rw[i] * acc[f][i]);
+    } else if (p.combine == 1) {
+      float* orow = p.out32 + (size_t)sid * p.H;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) orow[c0 + 16 * f] = rw[i] * acc[f][i];
+    } else {
+      float* orow = p.out32 + (size_t)(sid / p.k1) * p.H;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) atomicAdd(orow + c0 + 16 * f, rw[i] * acc[f][i]);
+    }
+  }
+}
+
+// Fused final rounding (atomic combine, small-M launcher): every wave that did a tile of column
+// chunk `chunk` bumps that chunk's counter once its atomics are acknowledged; the wave that
+// completes the count (one per tile with work) rounds the chunk's 64 columns of all T token rows
+// to bf16, reading the sums with agent-scope loads (the level the atomics are performed at). No
+// agent-scope fence is used: on this GPU it writes back and invalidates the whole L2 of the XCD,
+// which every wave of the pass would pay.
+__device__ __forceinline__ void finalize_chunk_if_last(const GemmParams& p, int chunk, int lane) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(p.chunk_done + chunk, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == *p.num_post_pad / p.block_m - 1;
+  last = __builtin_amdgcn_readfirstlane(last);
+  if (!last) return;
+  const int col = 64 * chunk + 4 * (lane & 15);
+  for (int t = lane >> 4; t < p.T; t += 4) {
+    float* src = p.out32 + (size_t)t * p.H + col;
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      v[c] = __hip_atomic_load(src + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint2 o;
+    o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *(uint2*)(p.y + (size_t)t * p.H + col) = o;
+  }
+}
+
 // ------------------------------------------------------------------------------ small-M
 template <int WF, int MT, bool GATE_UP, int D>
 __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, int n_blocks) {
+  static_assert(GATE_UP || MT == 1, "the down epilogue of this launcher handles one 16-row tile");
   const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
   // Unit order: XCD x = blockIdx % 8 takes the x-th contiguous range of units; units run
   // chunk-major, tiles fastest, so the tiles of one expert on one chunk share an XCD.
@@ -312,6 +367,17 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     Stage<WF, MT> buf[D];
 #pragma unroll
     for (int s = 0; s < D; ++s) load_b<WF, MT, MT>(p, tr, s, lane, buf[s]);
+    // down: slot id and routing weight of the lane's four output rows, fetched now so the
+    // epilogue does not wait for them
+    int rsid[4];
+    float rw[4];
+    if (!GATE_UP) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rsid[i] = p.sorted_ids[m0 + 4 * g + i];
+        rw[i] = rsid[i] < p.S ? p.topk_w[rsid[i]] : 0.f;
+      }
+    }
     tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
 #pragma unroll
     for (int s = 0; s < D; ++s) load_a<WF, MT>(tr, s, buf[s]);
@@ -325,9 +391,10 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     }
 #pragma unroll
     for (int s = 0; s < D; ++s) mma_stage<WF, MT>(buf[s], 8 * g, acc);
-    if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
-    else epilogue_down<MT>(p, acc, m0, r1, chunk, n, g);
+    if constexpr (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
+    else epilogue_down_rows(p, acc[0], rsid, rw, chunk, n);
   }
+  if (!GATE_UP && p.y) finalize_chunk_if_last(p, chunk, lane);
 }
 
 // ------------------------------------------------------------------------------ large-M
@@ -531,7 +598,7 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
       constexpr int H = FB / 1024;
       const int f = (q - 6) / H, h = (q - 6) % H;
       lds_load16(rw, st + L::b + (4 * wave + f) * FB + 1024 * h, (16u * lane + 1024u * h) | oob,
-                 ((nt0 + f) * p.NKS + ks) * FB);
+                 (((nt0 >> 2) * p.NKS + ks) * 4 + f) * FB);
     }
   };
   auto issue = [&](int stage, int ks, uint32_t oob) {

@@ -44,6 +44,8 @@ struct PrologueArgs {
   uint8_t* xs;
   int srs;
   float* zero_out;  // null: nothing to clear
+  int32_t* zero_cnt;  // n_cnt counters to clear (null: none)
+  int n_cnt;
 };
 hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_scratch,
                            hipStream_t st);
@@ -99,6 +101,11 @@ struct GemmParams {
   float* out32;              // slot rows [S, H] or token rows [T, H]
   int H;
   int combine;               // 1 fp32 slot rows, 2 fp32 atomics, 3 bf16 slot rows
+  // fused final rounding (small-M launcher with the atomic combine): y != null; chunk_done holds
+  // one completion counter per 64-column chunk, cleared by the prologue
+  uint16_t* y;
+  int32_t* chunk_done;
+  int T;
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);

@@ -11,9 +11,11 @@
 //   MXFP4 (1 KiB): [lane l][16 B]; lane l holds row n, K = 32g..32g+31, low nibble first.
 //   bf16  (4 KiB): [sub-step s][lane l][16 B]; lane l holds row n, K = 32s+8g..32s+8g+7 (the
 //                  v_mfma_f32_16x16x32_bf16 operand order, four per 128-K step).
-// Fragments of an expert are ordered [16-row tile nt][K-step ks]. For W13 the tiles alternate gate
-// and up: tile 2p holds gate rows 16p..16p+15 and tile 2p+1 up rows I+16p..I+16p+15, so one wave
-// holds matching gate and up columns for the SwiGLU epilogue.
+// Fragments of an expert are ordered [group of four tiles q][K-step ks][tile 4q + f]: the four
+// fragments one wave multiplies in a K-step are adjacent, so a wave streams its weights as one
+// contiguous range. For W13 the tiles alternate gate and up: tile 2p holds gate rows 16p..16p+15
+// and tile 2p+1 up rows I+16p..I+16p+15, so one wave holds matching gate and up columns for the
+// SwiGLU epilogue.
 // Scales: per (expert, group of four tiles q, K-step ks) 64 dwords; byte f of lane l = n + 16g is
 // the scale of row n of tile 4q + f for K-block 4ks + g. One dword load per lane and K-step serves
 // the four fragments a wave multiplies (the MFMA's scale operand selects byte f). K is zero-padded
@@ -43,10 +45,13 @@ __global__ __launch_bounds__(256) void k_prepack_codes(const uint8_t* src, uint8
   if (chunk >= total) return;
   int c = (int)(chunk % CH);
   size_t frag = chunk / CH;
-  int ks = (int)(frag % NKS);
-  size_t en = frag / NKS;
-  int nt = (int)(en % NT);
-  size_t e = en / NT;
+  const int f = (int)(frag & 3);
+  size_t r = frag >> 2;
+  int ks = (int)(r % NKS);
+  size_t eq = r / NKS;
+  const int NQ = NT / 4;
+  int nt = 4 * (int)(eq % NQ) + f;
+  size_t e = eq / NQ;
   int l, kin;  // lane, first K index (within the step) of this chunk
   if (WF == WF_FP8) {
     int h = c >> 6;

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
     __shared__ AlignSmem sm;
     __shared__ int32_t ids_lds[kAlignSmallMaxSlots];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.zero_cnt[i] = 0;
     route_tokens_any<F32>(a.logits, wave, kThreads / 64, a.T, a.E, a.top_k, lane, a.ids, a.w,
                           ids_lds);
     __syncthreads();
@@ -48,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
 template <bool F32>
 __global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_route) {
   if ((int)blockIdx.x < n_route) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.zero_cnt[i] = 0;
     const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (t < a.T)
       route_tokens_any<F32>(a.logits, t, a.T, a.T, a.E, a.top_k, threadIdx.x & 63, a.ids, a.w,
