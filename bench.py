@@ -176,7 +176,7 @@ def measure(name, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(g, n_tokens):
+def cpu_baseline(g, n_tokens, min_seconds=10.0):
     """The fp64 oracle on a bounded sample: n_tokens tokens of the same workload. Weight codes are
     produced before the timed region (load-time work); the timed region is the block itself:
     routing, sort, Q1, explicit per-expert MX dequantisation, fp64 GEMMs, SwiGLU, Q2, combine."""
@@ -194,10 +194,12 @@ def cpu_baseline(g, n_tokens):
     ids, _ = moe.route(lg[toks], w.top_k)
     need = sorted(set(ids.reshape(-1).tolist()))
     el = {"mxfp8": "e4m3", "mxfp4": "e2m1"}.get(w.w_fmt)
-    coded = {}
-    for e in need:                                    # untimed: load-time quantisation
+    def prep(e):                                      # untimed: load-time quantisation
         a, b = workloads.draw_expert(w, e)
-        coded[e] = (mx.quantize(a, el), mx.quantize(b, el)) if el else (a, b)
+        return e, ((mx.quantize(a, el), mx.quantize(b, el)) if el else (a, b))
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        coded = dict(ex.map(prep, need))
 
     def get(e):
         if not el:
@@ -205,17 +207,23 @@ def cpu_baseline(g, n_tokens):
         (c13, s13), (c2, s2) = coded[e]
         return mx.dequantize(c13, s13, el), mx.dequantize(c2, s2, el)
     W = moe.ExpertWeights(w.E, w.H, w.I, w.w_fmt, get, cache=0)
-    t0 = time.perf_counter()
-    r = moe.moe_block(x[toks], lg[toks], W, w.top_k, w.act_fmt)
-    moe.align(r.ids, w.E, 16)
-    sec = time.perf_counter() - t0
+    # the sample is repeated until about min_seconds of CPU work have been timed
+    reps, total = 0, 0.0
+    while reps < 1 or (total < min_seconds and reps < 200):
+        t0 = time.perf_counter()
+        r = moe.moe_block(x[toks], lg[toks], W, w.top_k, w.act_fmt)
+        moe.align(r.ids, w.E, 16)
+        total += time.perf_counter() - t0
+        reps += 1
+    sec = total / reps
     by = len(need) * expert_bytes(w) + len(toks) * (4 * w.H + 2 * w.E)
     y = g.y.float().cpu().numpy().astype(np.float64)[toks]
     par = moe.parity_stats(y, r.y)
     return {"value": by / sec / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": sec, "gflops": 6.0 * w.H * w.I * (w.top_k + 1) * len(toks) / sec / 1e9,
-            "sample": f"{len(toks)} of {w.T} tokens of {w.name} ({len(need)} experts touched); "
-                      f"fp64 numpy, same process and host",
+            "sample": f"{len(toks)} of {w.T} tokens of {w.name} ({len(need)} experts touched), "
+                      f"timed {reps} times ({total:.1f} s of CPU work); fp64 numpy, same process "
+                      f"and host",
             "parity_vs_gpu_on_sample": par}
 
 
@@ -242,6 +250,9 @@ def main():
                     help="comma-separated extra workloads, 'all', or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first run three device-to-device copies of this many MiB (a plain copy "
+                         "kernel of known size, to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block runs on one GPU's share of the tensor-parallel "
@@ -254,6 +265,16 @@ def main():
         sys.exit(2)
     from mx_quantized_grouped_amd import binding as B
     B.lib()
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.calibrate_copy_mb} MiB device-to-device")
+        del src, dst
+        torch.cuda.empty_cache()
     g, head = measure(args.workload, args.steps, args.warmup)
     others = {}
     extra = [] if args.extra == "none" else (

@@ -36,6 +36,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Sum over the 64 lanes of the wave, returned to every lane (same DPP pattern; rows outside a
+// broadcast's row mask add zero).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  auto add = [](float x, int y) { return x + __int_as_float(y); };
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppQuadPerm1032, 0xF, 0xF, false));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppQuadPerm2301, 0xF, 0xF, false));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor4, 0xF, 0xF, false));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowRor8, 0xF, 0xF, false));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+  v = add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ uint32_t route_order_key(uint32_t u) {
   if ((u & 0x7FFFFFFFu) == 0) u = 0;  // -0 == +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -99,11 +112,9 @@ __device__ void route_select(uint32_t (&vkey)[NPER], int t, int E, int top_k, in
   }
   float v = F32 ? route_key_value(mine_v)
                 : __uint_as_float(__float_as_uint(route_key_value(mine_v & 0xFFFF0000u)) & 0xFFFF0000u);
-  float v0 = __shfl(v, 0);
-  float p = lane < top_k ? expf(v - v0) : 0.f;
-  float s = p;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float p = lane < top_k ? expf(v - v0) : 0.f;
+  const float s = wave_sum_f32(p);
   const int k1 = top_k + 1;
   int32_t id = -1;
   float wt = 0.f;
