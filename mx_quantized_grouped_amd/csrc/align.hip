@@ -98,15 +98,16 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
   }
 }
 
-// Pass 3: sorted_ids[start(chunk, e) + rank] = f.
+// Pass 3: sorted_ids[start(chunk, e) + rank] = f (and the slot's weight into sorted_w).
 __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const int32_t* ids, int S, int E1,
                                                                  const int32_t* rank_in,
-                                                                 const int32_t* start,
-                                                                 int32_t* sorted_ids) {
+                                                                 const int32_t* start, AlignOut o) {
   int f = blockIdx.x * kAlignThreads + threadIdx.x;
   int e = align_expert_of(ids, f, S, E1);
   if (e < 0) return;
-  sorted_ids[start[(size_t)blockIdx.x * E1 + e] + rank_in[f]] = f;
+  const int pos = start[(size_t)blockIdx.x * E1 + e] + rank_in[f];
+  o.sorted_ids[pos] = f;
+  if (o.sorted_w) o.sorted_w[pos] = o.topk_w[f];
 }
 
 }  // namespace
@@ -126,12 +127,9 @@ size_t align_scratch_bytes(int T, int E, int top_k) {
 }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
-                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
-                        int32_t* expert_off, int32_t* touched, int32_t* n_touched, void* scratch,
-                        hipStream_t st) {
+                        const AlignOut& o, void* scratch, hipStream_t st) {
   const int S = T * (top_k + 1), E1 = E + 1;
   const int cap = (int)align_cap(S, E1, block_m);
-  AlignOut o{sorted_ids, block_expert, num_post_pad, expert_off, touched, n_touched};
   if (S <= kAlignSmallMaxSlots) {
     hipLaunchKernelGGL(k_align_small, dim3(1), dim3(kAlignThreads), 0, st, ids, S, E1, block_m,
                        cap, o);
@@ -146,7 +144,7 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m
   hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, start, nch, S, E1,
                      block_m, cap, o);
   hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank,
-                     start, sorted_ids);
+                     start, o);
   return hipGetLastError();
 }
 

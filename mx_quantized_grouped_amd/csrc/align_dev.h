@@ -104,8 +104,14 @@ inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1
     for (int e = t; e <= E1; e += kAlignThreads) o.expert_off[e] = off[e];
   // padding of each expert's run, then the unused tail
   for (int e = t; e < E1; e += kAlignThreads)
-    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) o.sorted_ids[r] = S;
-  for (int r = total + t; r < cap; r += kAlignThreads) o.sorted_ids[r] = S;
+    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) {
+      o.sorted_ids[r] = S;
+      if (o.sorted_w) o.sorted_w[r] = 0.f;
+    }
+  for (int r = total + t; r < cap; r += kAlignThreads) {
+    o.sorted_ids[r] = S;
+    if (o.sorted_w) o.sorted_w[r] = 0.f;
+  }
   // expert of every tile: binary search of the tile start in off[]
   const int nb = cap / bm;
   for (int b = t; b < nb; b += kAlignThreads) {
@@ -153,6 +159,7 @@ inline __device__ void align_small_body(const int32_t* ids, int S, int E1, int b
       int rank = __popcll(b[f >> 6] & ((1ull << (f & 63)) - 1ull));
       for (int w = 0; w < (f >> 6); ++w) rank += __popcll(b[w]);
       o.sorted_ids[sm.off[e] + rank] = f;
+      if (o.sorted_w) o.sorted_w[sm.off[e] + rank] = o.topk_w[f];
     }
     return;
   }
@@ -179,7 +186,9 @@ inline __device__ void align_small_body(const int32_t* ids, int S, int E1, int b
     if (e >= 0) {
       int before = 0;
       for (int w = 0; w < wave; ++w) before += sm.wcnt[w][e];
-      o.sorted_ids[sm.off[e] + sm.run[e] + before + rank] = f;
+      const int pos = sm.off[e] + sm.run[e] + before + rank;
+      o.sorted_ids[pos] = f;
+      if (o.sorted_w) o.sorted_w[pos] = o.topk_w[f];
     }
     __syncthreads();
     for (int x = t; x < E1; x += kAlignThreads) {

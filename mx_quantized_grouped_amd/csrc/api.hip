@@ -61,7 +61,7 @@ int check_shape(const mxmoe_shape* s) {
 
 enum Seg {
   SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF, SEG_TOUCHED, SEG_ALIGN,
-  SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, SEG_DONE, NSEG
+  SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, SEG_DONE, SEG_SORTW, NSEG
 };
 
 struct Plan {
@@ -115,6 +115,7 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   sz[SEG_H] = (size_t)p.cap * p.Ip * (p.mx ? 1 : 2);
   sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
   sz[SEG_DONE] = p.fuse_final ? (size_t)(p.H / 64) * 4 : 0;
+  sz[SEG_SORTW] = (size_t)p.cap * 4;
   sz[SEG_OUT] = p.combine == MXMOE_COMBINE_ATOMIC ? (size_t)p.T * p.H * 4
                                                   : (size_t)p.S * p.H * (p.combine == MXMOE_COMBINE_SLOTS ? 4 : 2);
   size_t at = 0;
@@ -178,9 +179,8 @@ int mxmoe_align(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
   size_t need = align_scratch_bytes(T, E, top_k);
   if (need && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
     return MXMOE_EWORKSPACE;
-  return hip_status(launch_align(topk_ids, T, E, top_k, block_m, sorted_ids, block_expert,
-                                 num_post_pad, expert_off, nullptr, nullptr, workspace,
-                                 (hipStream_t)stream));
+  AlignOut o{sorted_ids, block_expert, num_post_pad, expert_off, nullptr, nullptr, nullptr, nullptr};
+  return hip_status(launch_align(topk_ids, T, E, top_k, block_m, o, workspace, (hipStream_t)stream));
 }
 
 int mxmoe_quantize(const void* src, int rows, int K, int src_dtype, int fmt, uint8_t* codes,
@@ -282,6 +282,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   uint8_t* hs = (uint8_t*)(ws + P.off[SEG_HS]);
   float* out32 = (float*)(ws + P.off[SEG_OUT]);
   int32_t* done = (int32_t*)(ws + P.off[SEG_DONE]);
+  float* sorted_w = (float*)(ws + P.off[SEG_SORTW]);
   const bool slots = P.combine != MXMOE_COMBINE_ATOMIC;
 
   if (getenv("MXMOE_TRACE"))
@@ -303,7 +304,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   pa.w = tw;
   pa.block_m = P.bm;
   pa.cap = P.cap;
-  pa.out = AlignOut{sorted, bexp, counters, eoff, touched, counters + 1};
+  pa.out = AlignOut{sorted, bexp, counters, eoff, touched, counters + 1, tw, sorted_w};
   pa.x = (const uint16_t*)x;
   pa.H = P.H;
   pa.xq = P.mx ? xq : nullptr;
@@ -332,6 +333,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.h_stride = P.Ip * (P.mx ? 1 : 2);
   g.h_srs = P.srs_I;
   g.topk_w = tw;
+  g.sorted_w = sorted_w;
   g.out32 = out32;
   g.combine = P.combine;
   g.T = P.T;

@@ -21,6 +21,7 @@
 // the same XCD (workgroups go round-robin over the 8 XCDs, each with its own L2): an expert with
 // more than one tile reads its weights from HBM once, the grouped-MoE program ordering of the
 // MiniMax-M3 page's local-shapes passage.
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -263,7 +264,7 @@ __device__ __forceinline__ void epilogue_down(const GemmParams& p, const v4f (&a
       if (rr >= r1) continue;
       const int sid = p.sorted_ids[rr];
       if (sid >= p.S) continue;
-      const float wt = p.topk_w[sid];
+      const float wt = p.sorted_w[rr];
       const int c0 = 64 * chunk + n;
       if (p.combine == 3) {
         uint16_t* orow = (uint16_t*)p.out32 + (size_t)sid * p.H;
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         rsid[i] = p.sorted_ids[m0 + 4 * g + i];
-        rw[i] = rsid[i] < p.S ? p.topk_w[rsid[i]] : 0.f;
+        rw[i] = p.sorted_w[m0 + 4 * g + i];
       }
     }
     tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
@@ -553,9 +554,8 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   __shared__ __attribute__((aligned(16))) int row_sid[kTileM];
   __shared__ __attribute__((aligned(16))) float row_w[kTileM];
   if (!GATE_UP && tid < kTileM) {
-    const int sid = p.sorted_ids[r0 + tid];
-    row_sid[tid] = sid;
-    row_w[tid] = sid < p.S ? p.topk_w[sid] : 0.f;
+    row_sid[tid] = p.sorted_ids[r0 + tid];
+    row_w[tid] = p.sorted_w[r0 + tid];
   }
   const size_t wbytes = (size_t)p.NT * p.NKS * FB;
   const size_t sbytes = (size_t)(p.NT / 4) * p.NKS * 256;

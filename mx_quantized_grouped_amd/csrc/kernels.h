@@ -23,12 +23,14 @@ struct AlignOut {
   int32_t* expert_off;  // may be null
   int32_t* touched;     // may be null
   int32_t* n_touched;   // may be null
+  // optional: the routing weight of each sorted row (topk_w[sorted_ids[r]], 0 for padding), so the
+  // down pass reads a row's weight by row index instead of through its slot id
+  const float* topk_w;  // null: no sorted_w
+  float* sorted_w;
 };
 size_t align_scratch_bytes(int T, int E, int top_k);
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
-                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
-                        int32_t* expert_off, int32_t* touched, int32_t* n_touched, void* scratch,
-                        hipStream_t st);
+                        const AlignOut& o, void* scratch, hipStream_t st);
 
 // prologue.hip: route + sort + activation quantisation (or accumulator clearing) for forward.
 struct PrologueArgs {
@@ -98,6 +100,7 @@ struct GemmParams {
   int h_stride, h_srs, I, Ip;
   // down epilogue
   const float* topk_w;
+  const float* sorted_w;     // routing weight of each sorted row (0 for padding rows)
   float* out32;              // slot rows [S, H] or token rows [T, H]
   int H;
   int combine;               // 1 fp32 slot rows, 2 fp32 atomics, 3 bf16 slot rows

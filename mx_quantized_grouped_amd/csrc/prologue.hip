@@ -94,9 +94,7 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
   else hipLaunchKernelGGL(k_route_quant<false>, grid, block, 0, st, a, nr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_align(a.ids, a.T, a.E, a.top_k, a.block_m, a.out.sorted_ids, a.out.block_expert,
-                      a.out.num_post_pad, a.out.expert_off, a.out.touched, a.out.n_touched,
-                      align_scratch, st);
+  return launch_align(a.ids, a.T, a.E, a.top_k, a.block_m, a.out, align_scratch, st);
 }
 
 }  // namespace mxmoe
