@@ -401,35 +401,25 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
 // ------------------------------------------------------------------------------ large-M
 // Prefill launcher: a workgroup of 4 waves computes a 128-row x 256-column tile (rows of one expert
 // from the sorted layout); each wave owns 64 columns (4 weight fragments) for all 128 rows, i.e.
-// 8 x 4 block-scaled MFMAs per 128-K step.
+// 8 x 4 block-scaled MFMAs per 128-K step, with the 128 fp32 accumulators in AGPRs.
 //
-// Every operand of a K-step travels global -> LDS by the buffer unit's direct LDS loads (no
-// staging registers): the gathered 128 x 128-byte activation tile, the tile's activation scales,
-// each wave's 4 weight fragments and their scale dwords. LDS holds three stages, so the loads of
-// step ks + 2 are in flight while step ks is multiplied. A direct LDS load writes lane i's bytes
-// at (base + size * i), so the global address each lane requests decides the LDS layout:
-//   * activation rows are 128 bytes with the eight 16-byte units of row r stored at unit
-//     c ^ (r & 7) — the 16 rows an MFMA operand read touches then spread over all banks (measured
-//     on gfx950: ~198 B/clk/CU for this read pattern, against ~119 with 16-byte row padding);
-//   * weight fragments keep their prepacked [half][lane][16 B] order (contiguous reads).
-// Stage completion is a wait on the wave's own load counter followed by a workgroup barrier; it is
-// written as one asm statement because the compiler's barrier would first wait for all
-// outstanding loads, including the next stage's.
+// The gathered 128 x 128-byte activation tile of a K-step (and its scale dwords) is shared by the
+// 4 waves, so it travels global -> LDS by the buffer unit's direct LDS loads, double-buffered. The
+// weight fragments are private to a wave and go straight into registers (two slots, one K-step
+// ahead): staging them through LDS too doubled the LDS traffic and tripled the stage size. A
+// direct LDS load writes lane i's bytes at (base + size * i), so the global address each lane
+// requests decides the LDS layout: activation rows are 128 bytes with the eight 16-byte units of
+// row r stored at unit c ^ (r & 7) — the 16 rows an MFMA operand read touches then spread over all
+// banks (measured on gfx950: ~198 B/clk/CU for this read pattern, against ~119 with 16-byte row
+// padding). Stages are 17 KB and the kernel stays within 256 registers, so two workgroups share a
+// CU and each one's load waits are covered by the other's MFMAs (measured on the 8K-token
+// prefill: gate_up 274 us, down 253 us, against 316 / 312 us for one workgroup per CU with every
+// operand staged through a three-deep LDS ring).
+// Stage completion is a wait on the wave's own load counter followed by a workgroup barrier,
+// written as one asm statement (the compiler's barrier would also wait for loads it cannot see).
 constexpr int kTileM = 128;
 constexpr int kTileWaves = 4;
 constexpr int kLdsPitch = KSTEP;
-
-template <int WF>
-struct TileLds {
-  static constexpr int a = 0;                          // 128 rows x 128 B
-  static constexpr int as = kTileM * kLdsPitch;        // per wave 256 B of A scale dwords
-  static constexpr int bs = as + kTileWaves * 256;     // per wave 64 B scale dwords
-  static constexpr int b = bs + kTileWaves * 256;      // per wave 4 fragments
-  static constexpr int bytes = b + kTileWaves * 4 * Frag<WF>::bytes;
-  static constexpr int stages = 3;
-  // direct LDS loads per wave and K-step: 4 activation, 1 A scale, 1 B scale, the fragments
-  static constexpr int loads = 4 + 1 + 1 + 4 * Frag<WF>::bytes / 1024;
-};
 
 // Raw buffer descriptor words (same format as raw_rsrc) for the asm loads below.
 __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_bytes) {
@@ -462,11 +452,12 @@ __device__ __forceinline__ void wait_loads_barrier() {
 // code bytes go out as 16-byte stores (8 lanes per row) and its 4 scale bytes as one dword (the
 // scale layout is in K-block order). Rows of padding slots are written too (their codes are zero
 // since their activation rows read as zero), so the down pass can read every row of a tile.
-template <int WF>
+template <int WF, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const v4f (&acc)[8][4],
                                                       int r0, int chunk, int wave, int n, int g,
                                                       int tid, uint8_t* lds) {
   constexpr int kPitch = 128 + 16;           // code row pitch in LDS
+  static_assert(kTileM * kPitch + kTileM * 4 <= LDS_BYTES, "gate_up staging exceeds the LDS buffer");
   uint8_t* codes = lds;                      // [128][kPitch]
   uint32_t* scales = (uint32_t*)(lds + kTileM * kPitch);  // [128] dwords, byte = wave
 #pragma unroll
@@ -497,48 +488,64 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
 // down epilogue with bf16 slot rows: the tile's 128 x 256 bf16 products w(row) * d(row) are staged
 // in LDS (row pitch 512 + 32 bytes, so the four rows one store instruction touches fall in
 // different banks), then each slot row's 512-byte segment goes out as 16-byte stores (32 lanes per
-// row); rows of padding slots are skipped.
+// row); rows of padding slots are skipped. LDS_BYTES is the caller's LDS buffer size: the tile is
+// staged in as many passes of whole 16-row groups as that buffer needs (checked at compile time).
+template <int LDS_BYTES>
 __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4f (&acc)[8][4],
                                                    int r0, int chunk, int wave, int n, int g,
                                                    int tid, uint8_t* lds, const int* row_sid,
                                                    const float* row_w) {
   constexpr int kPitch = 512 + 32;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const v4f wt = *(const v4f*)(row_w + 16 * mt + 4 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t* orow = (uint16_t*)(lds + (16 * mt + 4 * g + i) * kPitch) + 64 * wave + n;
-#pragma unroll
-      for (int f = 0; f < 4; ++f) orow[16 * f] = (uint16_t)f32_to_bf16_bits(wt[i] * acc[mt][f][i]);
-    }
-  }
-  __syncthreads();
+  constexpr int kNeed = (kTileM * kPitch + LDS_BYTES - 1) / LDS_BYTES;
+  constexpr int kPasses = kNeed <= 1 ? 1 : (kNeed <= 2 ? 2 : (kNeed <= 4 ? 4 : 8));
+  constexpr int kRows = kTileM / kPasses;    // rows staged per pass
+  constexpr int kGroups = kRows / 16;        // 16-row MFMA groups per pass
+  static_assert(kRows * kPitch <= LDS_BYTES, "down epilogue staging exceeds the LDS buffer");
+  static_assert(kRows * 32 % 256 == 0, "copy-out assumes whole rounds of 256 threads");
   uint16_t* out16 = (uint16_t*)p.out32;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass) __syncthreads();  // the previous pass's rows have been copied out
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int mt = pass * kGroups + q;
+      const v4f wt = *(const v4f*)(row_w + 16 * mt + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t* orow = (uint16_t*)(lds + (16 * q + 4 * g + i) * kPitch) + 64 * wave + n;
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          orow[16 * f] = (uint16_t)f32_to_bf16_bits(wt[i] * acc[mt][f][i]);
+      }
+    }
+    __syncthreads();
 #pragma unroll 4
-  for (int j = 0; j < 16; ++j) {
-    const int c = tid + 256 * j, row = c >> 5, unit = c & 31;
-    const int sid = row_sid[row];
-    if (sid < p.S)
-      *(v4i*)(out16 + (size_t)sid * p.H + 256 * chunk + 8 * unit) =
-          *(const v4i*)(lds + row * kPitch + 16 * unit);
+    for (int j = 0; j < kRows * 32 / 256; ++j) {
+      const int c = tid + 256 * j, lrow = c >> 5, unit = c & 31;
+      const int sid = row_sid[pass * kRows + lrow];
+      if (sid < p.S)
+        *(v4i*)(out16 + (size_t)sid * p.H + 256 * chunk + 8 * unit) =
+            *(const v4i*)(lds + lrow * kPitch + 16 * unit);
+    }
   }
 }
 
+// LDS stage of the large-M launcher: the 128 x 128-byte activation tile and its scale dwords
+// (per wave 256 bytes; waves 2 and 3 fill an unused slot, see below).
+struct TileLds {
+  static constexpr int a = 0;
+  static constexpr int as = kTileM * kLdsPitch;
+  static constexpr int bytes = as + kTileWaves * 256;
+};
+
 template <int WF, bool GATE_UP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
-  using L = TileLds<WF>;
+  using L = TileLds;
   constexpr int MT = kTileM / 16;
-  constexpr int FB = Frag<WF>::bytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::stages * L::bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * L::bytes];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
-  // wave-uniform by construction; readfirstlane tells the compiler, so the scalar offsets and LDS
-  // addresses of the loads below stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Unit order: each XCD takes a contiguous range of units, tile-major with the column chunks of a
-  // tile adjacent — the gathered activation tile is fetched once into that XCD's L2 and reused by
-  // its column chunks, and an expert's consecutive tiles reuse its weight slices from L2.
   const int total = n_chunks * n_blocks;
   const int per_xcd = (total + 7) >> 3;
   const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -547,25 +554,17 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   const int r0 = blk * kTileM;
   if (r0 >= *p.num_post_pad) return;
   const int e = p.block_expert[blk];
-  const int r1 = r0 + kTileM;
-  const int wchunk = chunk * kTileWaves + wave;  // this wave's 64-column chunk
-  const int nt0 = wchunk * 4;
-  // down: slot id and routing weight of each tile row, for the combine epilogue
+  const int wchunk = chunk * kTileWaves + wave;
+  TileRows<1> tr;
+  tile_weights<WF, 1>(p, e, wchunk * 4, tr);
   __shared__ __attribute__((aligned(16))) int row_sid[kTileM];
   __shared__ __attribute__((aligned(16))) float row_w[kTileM];
   if (!GATE_UP && tid < kTileM) {
     row_sid[tid] = p.sorted_ids[r0 + tid];
     row_w[tid] = p.sorted_w[r0 + tid];
   }
-  const size_t wbytes = (size_t)p.NT * p.NKS * FB;
-  const size_t sbytes = (size_t)(p.NT / 4) * p.NKS * 256;
-  const v4i rw = rsrc_words(p.w + (size_t)e * wbytes, (uint32_t)wbytes);
-  const v4i rws = rsrc_words(p.ws + (size_t)e * sbytes, (uint32_t)sbytes);
   const v4i ra = rsrc_words(p.a, p.a_bytes);
   const v4i ras = rsrc_words(p.as, p.as_bytes);
-
-  // Source row offsets. Activation load j of this wave fills tile rows 32 wave + 8 j + lane / 8;
-  // the lane fetches the unit that belongs at LDS unit lane % 8 of that row.
   auto act_row = [&](int r, uint32_t stride) -> uint32_t {
     if (GATE_UP) {
       const int sid = p.sorted_ids[r];
@@ -578,101 +577,73 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   for (int j = 0; j < 4; ++j)
     aoff[j] = act_row(r0 + 32 * wave + 8 * j + (lane >> 3), (uint32_t)p.a_stride) +
               16u * ((lane & 7) ^ (lane >> 3));
-  // A scale dwords: waves 0 and 1 fetch rows 64 wave + lane; waves 2 and 3 issue the same load
-  // out of range (zeros into their own unused slot), so every wave counts the same loads.
   const uint32_t asoff = wave < 2 ? act_row(r0 + 64 * wave + lane, (uint32_t)p.a_srs) : kOutOfRange;
-  const int bs_base = (nt0 >> 2) * p.NKS * 256;
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
-
-  // Load q (0 .. L::loads - 1) of a K-step: 0-3 activation rows, 4 A scales, 5 B scales, then the
-  // weight fragments. oob = kOutOfRange turns it into an out-of-range load (it writes zeros and
-  // moves no data), so steps past the end still issue the same number of loads.
-  auto issue_one = [&](int q, uint32_t st, int ks, uint32_t oob) {
-    if (q < 4) {
-      lds_load16(ra, st + L::a + (32 * wave + 8 * q) * kLdsPitch, aoff[q] | oob, ks * KSTEP);
-    } else if (q == 4) {
-      lds_load4(ras, st + L::as + 256 * wave, asoff | oob, 4 * ks);
-    } else if (q == 5) {
-      lds_load4(rws, st + L::bs + 256 * wave, (4u * lane) | oob, bs_base + ks * 256);
-    } else {
-      constexpr int H = FB / 1024;
-      const int f = (q - 6) / H, h = (q - 6) % H;
-      lds_load16(rw, st + L::b + (4 * wave + f) * FB + 1024 * h, (16u * lane + 1024u * h) | oob,
-                 (((nt0 >> 2) * p.NKS + ks) * 4 + f) * FB);
-    }
-  };
-  auto issue = [&](int stage, int ks, uint32_t oob) {
+  auto issue_a = [&](int stage, int ks, uint32_t oob) {
     const uint32_t st = lds0 + stage * L::bytes;
 #pragma unroll
-    for (int q = 0; q < L::loads; ++q) issue_one(q, st, ks, oob);
+    for (int j = 0; j < 4; ++j)
+      lds_load16(ra, st + L::a + (32 * wave + 8 * j) * kLdsPitch, aoff[j] | oob, ks * KSTEP);
+    lds_load4(ras, st + L::as + 256 * wave, asoff | oob, 4 * ks);
   };
-
   v4f acc[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // rows n + 16 mt share (row & 7) = n & 7, so the swizzled units are loop-invariant
   const int u0 = (g ^ (n & 7)) << 4, u1 = ((4 + g) ^ (n & 7)) << 4;
-  // Multiply the stage's tile while issuing the next-but-one step's loads, four of them before
-  // every other 16-row group, so that the load issue overlaps the matrix cores instead of
-  // preceding them (measured on the 8K-token prefill: 314 us for gate_up against 347 us with all
-  // loads issued at the start of the step).
-  auto compute_issue = [&](int stage, int nstage, int ks2, uint32_t oob) {
+  Stage<WF, 1> bs[2];
+  auto compute = [&](int stage, const Stage<WF, 1>& b, int mt0, int mt1) {
     const uint8_t* st = lds + stage * L::bytes;
-    const uint32_t nst = lds0 + nstage * L::bytes;
-    v4i b[4][2];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      b[f][0] = *(const v4i*)(st + L::b + (4 * wave + f) * FB + 16 * lane);
-      b[f][1] = WF == WF_FP8 ? *(const v4i*)(st + L::b + (4 * wave + f) * FB + 1024 + 16 * lane)
-                             : v4i{0, 0, 0, 0};
-    }
-    const int sb = *(const int*)(st + L::bs + 256 * wave + 4 * lane);
     const uint8_t* base = st + L::a + n * kLdsPitch;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = mt0; mt < mt1; ++mt) {
       v8i a8;
       a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
       a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
       const uint32_t sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
-      if (mt % 2 == 0) {
-#pragma unroll
-        for (int q = 2 * mt; q < 2 * mt + 4; ++q)
-          if (q < L::loads) issue_one(q, nst, ks2, oob);
-      }
-      mma_frags<WF>(a8, (int)(sa >> (8 * g)), b, sb, acc[mt]);
+      mma_frags<WF>(a8, (int)(sa >> (8 * g)), b.b, (int)b.sb, acc[mt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
-
-  // Step ks reads stage ks % 3. The loads of step ks + 2 go out first, into the stage step ks - 1
-  // read (every wave has passed the barrier after it); the barrier at the end of the step makes
-  // step ks + 1's stage complete for all waves while step ks + 2's loads stay in flight. The body
-  // has no branch (steps past the end issue out-of-range loads), and a scheduling barrier keeps
-  // the MFMAs ahead of the wait.
   const int nks = p.NKS;
-  issue(0, 0, 0u);
-  issue(1, 1, nks > 1 ? 0u : kOutOfRange);
-  wait_loads_barrier<L::loads>();
-  static_assert(L::loads <= 2 * MT, "loads must fit the 16-row groups");
-  int stage = 0;
-  for (int ks = 0; ks < nks; ++ks) {
-    compute_issue(stage, stage == 0 ? 2 : stage - 1, ks + 2, ks + 2 < nks ? 0u : kOutOfRange);
-    wait_loads_barrier<L::loads>();
-    stage = stage == 2 ? 0 : stage + 1;
-  }
-  // the last steps' out-of-range loads still write zeros into LDS: drain them in every wave
+  const int nks2 = (nks + 1) & ~1;  // padded to even: a trailing step of zeros
+  load_b<WF, 1, 1>(p, tr, 0, lane, bs[0]);
+  issue_a(0, 0, 0u);
   wait_loads_barrier<0>();
-  // Every wave has passed the last barrier, so the stage buffers are free: the epilogues stage the
-  // output tile there and write whole rows with 16-byte stores (the per-lane MFMA layout holds one
-  // column of four rows, which stored directly means 1- or 2-byte scattered stores).
+  // Step ks multiplies stage / weight slot ks % 2. The loads of step ks + 1 go out while it runs:
+  // the activation tile (no registers) after the first two 16-row groups, the weights after the
+  // sixth (earlier, both weight slots would be live across the MFMAs and the fp8 kernel would
+  // spill). By then the compiler has waited for this step's weights, so its count of outstanding
+  // loads cannot make it wait for the new ones (the activation loads are invisible to it). The
+  // loop runs over pairs of steps so that the register slots are compile-time; an odd step count
+  // gets a trailing step of zeros (out-of-range loads).
+  auto step = [&](auto SLOT, int ks) {
+    constexpr int s = decltype(SLOT)::value;
+    const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
+    compute(s, bs[s], 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(1 - s, ks + 1, oob);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, bs[s], 2, 6);
+    __builtin_amdgcn_sched_barrier(0);
+    TileRows<1> tn = tr;
+    if (oob) tn.w = raw_rsrc(p.w, 0);
+    load_b<WF, 1, 1>(p, tn, ks + 1 < nks ? ks + 1 : 0, lane, bs[1 - s]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, bs[s], 6, MT);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_loads_barrier<0>();
+  };
+  for (int ks = 0; ks < nks2; ks += 2) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
+  }
   if constexpr (GATE_UP) {
-    epilogue_gate_up_tile<WF>(p, acc, r0, chunk, wave, n, g, tid, lds);
+    epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds);
   } else {
-    if (p.combine == 3) epilogue_down_tile(p, acc, r0, chunk, wave, n, g, tid, lds, row_sid, row_w);
-    else epilogue_down<MT>(p, acc, r0, r1, wchunk, n, g);
+    if (p.combine == 3)
+      epilogue_down_tile<sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds, row_sid, row_w);
+    else epilogue_down<MT>(p, acc, r0, r0 + kTileM, wchunk, n, g);
   }
 }
 
