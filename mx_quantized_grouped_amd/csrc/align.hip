@@ -45,8 +45,13 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
 
 // Pass 2 (one workgroup): totals, padded offsets and layout outputs; start[c * E1 + e] becomes the
 // absolute start of the (chunk c, expert e) piece. Threads split into (expert, segment of chunks)
-// pairs so the chunk histograms are walked in parallel.
-__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist,
+// pairs so the chunk histograms are walked in parallel. When the histograms fit (up to 28 Ki
+// counts), they are first copied into LDS with coalesced loads issued in batches of 8 per thread
+// (a plain copy loop waits for each load before issuing the next: one memory latency per
+// iteration); walked in global memory, the per-thread chain of loads made this pass take 16 us
+// for an 8K-token batch.
+constexpr int kScanLdsCounts = 28 * 1024;
+__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
                                                               int32_t* __restrict__ start,
                                                               int nchunks, int S, int E1, int bm,
                                                               int cap, AlignOut o) {
@@ -54,7 +59,28 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
   __shared__ int off[kAlignMaxE1 + 1];
   __shared__ int s_wave[kAlignWaves];
   __shared__ int seg_sum[kAlignThreads];
+  __shared__ int hist_l[kScanLdsCounts];
   const int t = threadIdx.x;
+  const int nh = nchunks * E1;
+  const int32_t* hist = hist_g;
+  if (nh <= kScanLdsCounts) {
+    constexpr int kB = 8;
+    for (int base = t; base < nh; base += kB * kAlignThreads) {
+      int v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = base + j * kAlignThreads;
+        v[j] = i < nh ? hist_g[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = base + j * kAlignThreads;
+        if (i < nh) hist_l[i] = v[j];
+      }
+    }
+    __syncthreads();
+    hist = hist_l;
+  }
   const int P = E1 >= kAlignThreads ? 1 : kAlignThreads / E1;  // segments per expert
   const int seg = (nchunks + P - 1) / P;
   const int part = t / E1, e = t - part * E1;

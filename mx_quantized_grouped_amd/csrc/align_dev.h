@@ -47,15 +47,23 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid) {
   return mine;
 }
 
+// Inclusive scan over the 64 lanes of the wave with DPP: shifts by 1, 2, 4, 8 inside each 16-lane
+// row (lanes shifted in from outside the row add 0), then the row totals are carried by two row
+// broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive scan over the 1024-thread workgroup (one value each); also returns the total.
 __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   int before = 0, tot = 0;
@@ -102,30 +110,37 @@ inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1
   __syncthreads();
   if (o.expert_off)
     for (int e = t; e <= E1; e += kAlignThreads) o.expert_off[e] = off[e];
-  // padding of each expert's run, then the unused tail
-  for (int e = t; e < E1; e += kAlignThreads)
-    for (int r = off[e] + cnt[e]; r < off[e + 1]; ++r) {
-      o.sorted_ids[r] = S;
-      if (o.sorted_w) o.sorted_w[r] = 0.f;
+  // Padding of each expert's run and the expert of each of its tiles. With tall tiles (up to 255
+  // padding slots per expert) one wave takes an expert, so consecutive lanes write consecutive
+  // entries: a thread per expert makes every store instruction touch 64 cache lines (~20 us for
+  // the 8K-token layout at 128-row tiles). With short tiles a thread per expert is cheaper (a wave
+  // walking 8 experts in turn cost 2 us more at 16-row tiles).
+  if (bm > 32) {
+    const int lane = t & 63;
+    for (int e = t >> 6; e < E1; e += kAlignWaves) {
+      const int o0 = off[e], o1 = off[e + 1];
+      for (int r = o0 + cnt[e] + lane; r < o1; r += 64) {
+        o.sorted_ids[r] = S;
+        if (o.sorted_w) o.sorted_w[r] = 0.f;
+      }
+      for (int b = o0 / bm + lane; b < o1 / bm; b += 64) o.block_expert[b] = e;
     }
+  } else {
+    for (int e = t; e < E1; e += kAlignThreads) {
+      const int o0 = off[e], o1 = off[e + 1];
+      for (int r = o0 + cnt[e]; r < o1; ++r) {
+        o.sorted_ids[r] = S;
+        if (o.sorted_w) o.sorted_w[r] = 0.f;
+      }
+      for (int b = o0 / bm; b < o1 / bm; ++b) o.block_expert[b] = e;
+    }
+  }
   for (int r = total + t; r < cap; r += kAlignThreads) {
     o.sorted_ids[r] = S;
     if (o.sorted_w) o.sorted_w[r] = 0.f;
   }
-  // expert of every tile: binary search of the tile start in off[]
   const int nb = cap / bm;
-  for (int b = t; b < nb; b += kAlignThreads) {
-    int pos = b * bm, v = -1;
-    if (pos < total) {
-      int lo = 0, hi = E1 - 1;  // largest e with off[e] <= pos: the non-empty run holding pos
-      while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= pos) lo = mid; else hi = mid - 1;
-      }
-      v = lo;
-    }
-    o.block_expert[b] = v;
-  }
+  for (int b = total / bm + t; b < nb; b += kAlignThreads) o.block_expert[b] = -1;
 }
 
 // The whole sort in one 1024-thread workgroup (S small). ids may live in LDS or global memory.

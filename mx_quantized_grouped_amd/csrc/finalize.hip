@@ -8,6 +8,10 @@ namespace mxmoe {
 
 namespace {
 
+// Slot rows read per batch: all loads of a batch are issued before the first add (a loop that
+// adds each slot as it arrives waits one memory latency per slot).
+constexpr int kBatch = 9;
+
 // One thread per 8 consecutive output columns.
 template <int COMBINE>
 __global__ __launch_bounds__(256) void k_finalize(const void* out, int T, int H, int k1,
@@ -22,22 +26,38 @@ __global__ __launch_bounds__(256) void k_finalize(const void* out, int T, int H,
     const float* out32 = (const float*)out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s[i] = 0.f;
-    for (int j = 0; j < k1; ++j) {
-      const v4f* p = (const v4f*)(out32 + (t * k1 + j) * H + c);
-      v4f a = p[0], b = p[1];
-      s[0] += a[0]; s[1] += a[1]; s[2] += a[2]; s[3] += a[3];
-      s[4] += b[0]; s[5] += b[1]; s[6] += b[2]; s[7] += b[3];
+    for (int j0 = 0; j0 < k1; j0 += kBatch) {  // a batch of slot rows in flight, then the adds
+      v4f a[kBatch], b[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {  // indices past the last slot re-read it (added as zero)
+        const v4f* p = (const v4f*)(out32 + (t * k1 + min(j0 + q, k1 - 1)) * H + c);
+        a[q] = p[0];
+        b[q] = p[1];
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const float on = j0 + q < k1 ? 1.f : 0.f;
+        s[0] += on * a[q][0]; s[1] += on * a[q][1]; s[2] += on * a[q][2]; s[3] += on * a[q][3];
+        s[4] += on * b[q][0]; s[5] += on * b[q][1]; s[6] += on * b[q][2]; s[7] += on * b[q][3];
+      }
     }
   } else if (COMBINE == 3) {
     const uint16_t* out16 = (const uint16_t*)out;
 #pragma unroll
     for (int i = 0; i < 8; ++i) s[i] = 0.f;
-    for (int j = 0; j < k1; ++j) {
-      v4i q = *(const v4i*)(out16 + (t * k1 + j) * H + c);
+    for (int j0 = 0; j0 < k1; j0 += kBatch) {  // a batch of slot rows in flight, then the adds
+      v4i q[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[2 * i] += bf16_bits_to_f32((uint32_t)q[i] & 0xFFFFu);
-        s[2 * i + 1] += bf16_bits_to_f32((uint32_t)q[i] >> 16);
+      for (int b = 0; b < kBatch; ++b)  // indices past the last slot re-read it (added as zero)
+        q[b] = *(const v4i*)(out16 + (t * k1 + min(j0 + b, k1 - 1)) * H + c);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const bool on = j0 + b < k1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[2 * i] += on ? bf16_bits_to_f32((uint32_t)q[b][i] & 0xFFFFu) : 0.f;
+          s[2 * i + 1] += on ? bf16_bits_to_f32((uint32_t)q[b][i] >> 16) : 0.f;
+        }
       }
     }
   } else {

@@ -158,6 +158,25 @@ def test_align_random_shapes():
         assert np.array_equal(o.cpu().numpy(), L.expert_off)
 
 
+def test_align_large_histograms():
+    """Chunk histograms too large for the scan pass's LDS copy (73 chunks x 1025 experts): the
+    scan walks them in global memory. Routing rows are drawn directly (k distinct experts per
+    token, shared slot last) since only the layout is under test."""
+    _say("align large histograms")
+    rng = np.random.default_rng(11)
+    T, E, k, bm = 8300, 1024, 8, 64
+    rid = np.empty((T, k + 1), dtype=np.int64)
+    for t in range(T):
+        rid[t, :k] = rng.choice(E, size=k, replace=False)
+    rid[:, k] = E
+    L = moe.align(rid, E, bm)
+    s, b, n, o = B.mxmoe_align(torch.from_numpy(rid.astype(np.int32)).to(DEV), E, bm)
+    assert int(n.item()) == L.num_post_pad
+    assert np.array_equal(s.cpu().numpy(), L.sorted_ids)
+    assert np.array_equal(b.cpu().numpy(), L.block_expert)
+    assert np.array_equal(o.cpu().numpy(), L.expert_off)
+
+
 # ------------------------------------------------------------------------------- forward
 def _run_forward(name, options=None, logits_dtype="bf16"):
     w, xb, lb = inputs(name)
