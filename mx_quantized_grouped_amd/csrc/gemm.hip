@@ -606,7 +606,6 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
     }
   };
   const int nks = p.NKS;
-  const int nks2 = (nks + 1) & ~1;  // padded to even: a trailing step of zeros
   load_b<WF, 1, 1>(p, tr, 0, lane, bs[0]);
   issue_a(0, 0, 0u);
   wait_loads_barrier<0>();
@@ -615,8 +614,8 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   // sixth (earlier, both weight slots would be live across the MFMAs and the fp8 kernel would
   // spill). By then the compiler has waited for this step's weights, so its count of outstanding
   // loads cannot make it wait for the new ones (the activation loads are invisible to it). The
-  // loop runs over pairs of steps so that the register slots are compile-time; an odd step count
-  // gets a trailing step of zeros (out-of-range loads).
+  // loop runs over pairs of steps so that the register slots are compile-time; after an odd step
+  // count the last step runs alone (its loads were issued by the step before it).
   auto step = [&](auto SLOT, int ks) {
     constexpr int s = decltype(SLOT)::value;
     const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
@@ -634,10 +633,12 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
     __builtin_amdgcn_sched_barrier(0);
     wait_loads_barrier<0>();
   };
-  for (int ks = 0; ks < nks2; ks += 2) {
+  int ks = 0;
+  for (; ks + 1 < nks; ks += 2) {
     step(std::integral_constant<int, 0>{}, ks);
     step(std::integral_constant<int, 1>{}, ks + 1);
   }
+  if (ks < nks) compute(0, bs[0], 0, MT);  // odd step count: the last step alone (nothing to load)
   if constexpr (GATE_UP) {
     epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds);
   } else {
