@@ -611,9 +611,10 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   wait_loads_barrier<0>();
   // Step ks multiplies stage / weight slot ks % 2. The loads of step ks + 1 go out while it runs:
   // the activation tile (no registers) after the first two 16-row groups, the weights after the
-  // sixth (earlier, both weight slots would be live across the MFMAs and the fp8 kernel would
-  // spill). By then the compiler has waited for this step's weights, so its count of outstanding
-  // loads cannot make it wait for the new ones (the activation loads are invisible to it). The
+  // fourth (at 255 registers; issued after the second, both weight slots would be live across
+  // more MFMAs and the fp8 kernel spills). By then the compiler has waited for this step's
+  // weights, so its count of outstanding loads cannot make it wait for the new ones (the
+  // activation loads are invisible to it). The
   // loop runs over pairs of steps so that the register slots are compile-time; after an odd step
   // count the last step runs alone (its loads were issued by the step before it).
   auto step = [&](auto SLOT, int ks) {
@@ -623,13 +624,13 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
     __builtin_amdgcn_sched_barrier(0);
     issue_a(1 - s, ks + 1, oob);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s, bs[s], 2, 6);
+    compute(s, bs[s], 2, 4);
     __builtin_amdgcn_sched_barrier(0);
     TileRows<1> tn = tr;
     if (oob) tn.w = raw_rsrc(p.w, 0);
     load_b<WF, 1, 1>(p, tn, ks + 1 < nks ? ks + 1 : 0, lane, bs[1 - s]);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s, bs[s], 6, MT);
+    compute(s, bs[s], 4, MT);
     __builtin_amdgcn_sched_barrier(0);
     wait_loads_barrier<0>();
   };
