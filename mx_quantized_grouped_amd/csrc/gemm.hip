@@ -550,7 +550,13 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks) {
   const int per_xcd = (total + 7) >> 3;
   const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (u >= total) return;
-  const int blk = u / n_chunks, chunk = u - blk * n_chunks;
+  // Unit order inside an XCD's range: gate_up runs tile-major (the column chunks of a tile are
+  // adjacent, so the gathered activation tile is fetched once and reused from L2); down runs
+  // chunk-major (an expert's tiles on one column chunk are adjacent and reuse that weight slice
+  // from L2; measured: 8K-token down 218 -> 204 us, 512-expert 4K-token down 145 -> 100 us, no
+  // change for gate_up).
+  const int blk = GATE_UP ? u / n_chunks : u % n_blocks;
+  const int chunk = GATE_UP ? u - blk * n_chunks : u / n_blocks;
   const int r0 = blk * kTileM;
   if (r0 >= *p.num_post_pad) return;
   const int e = p.block_expert[blk];
