@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
     cnt[x] = s2;
   }
   __syncthreads();
-  align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o);
+  align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o, nullptr);
   __syncthreads();
   for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
     if (pass == 1 && (P != 1 || ee >= E1)) break;
