@@ -2,9 +2,9 @@
 // as the batch allows. Launch count matters at decode sizes, where every kernel node costs a few
 // microseconds ("Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell",
 // "Hai loại thời gian nhàn rỗi": hundreds of 1.5-6 us kernel nodes at batch 1).
-//   up to 16 tokens (and S <= 4096): one launch; workgroup 0 routes every token (one wave per
-//     token) into LDS and sorts the slots there, the other workgroups quantise x (and clear the
-//     atomic accumulator when that combine is used).
+//   up to 32 tokens (and S <= 4096): one launch; workgroup 0 routes every token (each wave takes
+//     at most two, back to back) into LDS and sorts the slots there, the other workgroups quantise
+//     x (and clear the atomic accumulator when that combine is used).
 //   more tokens: one launch routes (one wave per token, 16 per workgroup) and quantises, then the
 //     sort: one workgroup up to 4096 slots, the three-pass sort beyond.
 #include "align_dev.h"
@@ -79,10 +79,11 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
   const int S = a.T * (a.top_k + 1);
   const bool work = a.xq || a.zero_out;
   const int nq = work ? (int)(((size_t)a.T * (a.H / 32) + kThreads - 1) / kThreads) : 0;
-  // One launch while one workgroup routes every token with one wave each; beyond that, routing
-  // spreads over workgroups and the sort becomes a launch of its own (a wave routes a token in
-  // about 2 us, so the fused kernel would route T / 16 tokens per wave back to back).
-  if (S <= kAlignSmallMaxSlots && a.T <= kThreads / 64) {
+  // One launch while one workgroup's 16 waves route every token two at most each: a wave routes a
+  // token in about 1.7 us, so at 32 tokens the fused kernel (about 11.4 us) still beats a routing
+  // launch plus a sort launch (about 12.9 us with the gap between them); beyond that, routing
+  // spreads over workgroups and the sort becomes a launch of its own.
+  if (S <= kAlignSmallMaxSlots && a.T <= 2 * (kThreads / 64)) {
     dim3 grid(1 + nq), block(kThreads);
     if (logits_f32) hipLaunchKernelGGL(k_prologue_small<true>, grid, block, 0, st, a);
     else hipLaunchKernelGGL(k_prologue_small<false>, grid, block, 0, st, a);

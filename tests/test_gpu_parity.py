@@ -265,7 +265,8 @@ def test_forward_slots_deterministic_and_permutation_invariant():
     (1, 128, 1, 1, 32, "mxfp8"),      # one token, one routed expert
     (5, 256, 4, 4, 96, "mxfp8"),      # k == E; I not a multiple of 128 (padded K of down)
     (7, 384, 6, 2, 160, "mxfp4"),
-    (33, 128, 16, 3, 64, "bf16"),
+    (17, 256, 8, 2, 64, "mxfp8"),     # one-launch prologue with one wave routing two tokens
+    (33, 128, 16, 3, 64, "bf16"),     # just past the one-launch prologue
     (300, 256, 8, 2, 64, "mxfp8"),    # large-M launcher on a small problem
 ])
 def test_forward_edge_shapes(T, H, E, k, I, fmt):
