@@ -288,6 +288,31 @@ def test_forward_edge_shapes(T, H, E, k, I, fmt):
         assert tolerance_ok(st), (opt.launcher, opt.combine, st)
 
 
+# 256-row layout blocks on the large-M launcher (each block runs as two 128-row tiles): odd and
+# single K-step counts, fp8 and fp4 weights, experts with fewer rows than one block
+@pytest.mark.parametrize("T,H,E,k,I,fmt", [
+    (520, 384, 4, 2, 128, "mxfp8"),   # 3 K-steps: the step pairs end on a zero step
+    (300, 128, 4, 3, 256, "mxfp4"),   # 1 K-step
+    (700, 1024, 6, 2, 256, "mxfp8"),
+])
+def test_forward_wide_tiles(T, H, E, k, I, fmt):
+    _say("wide tiles", T, H, E, k, I, fmt)
+    wl = workloads.Workload(f"wide_{T}_{H}_{E}_{k}_{I}_{fmt}", T, H, E, k, I, fmt, "mxfp8", False, 5)
+    from mx_quantized_grouped_amd.weights import ExpertLoader
+    shape = shape_of(wl)
+    loader = ExpertLoader(shape, DEV)
+    for e in range(E + 1):
+        loader.add_expert(e, *workloads.draw_expert(wl, e))
+    packed = loader.finish()
+    xb, lb = workloads.draw_x(wl), workloads.draw_logits(wl)
+    ref = moe.moe_block(f64(xb), f64(lb), oracle_weights(wl), k, wl.act_fmt)
+    for opt in [B.Options(2, 3, 256, 0), B.Options(2, 1, 256, 0)]:
+        y = B.mxmoe_forward(shape, bf16_tensor(xb), bf16_tensor(lb), packed, options=opt)
+        torch.cuda.synchronize()
+        st = moe.parity_stats(y.float().cpu().numpy(), ref.y)
+        assert tolerance_ok(st), (opt.combine, st)
+
+
 def test_forward_zero_tokens_is_noop():
     shape = B.Shape.of(0, 256, 8, 2, 128, "mxfp8")
     assert B.lib().mxmoe_forward(shape, None, None, None, None, None, None, None, None, 0,
