@@ -1,6 +1,9 @@
 // moe_align kernels (the counting sort itself is described in align_dev.h). Two variants:
 //   small (S <= 4096): one workgroup does count, scan, padding and scatter;
-//   large: per-chunk counts + in-chunk ranks, one-workgroup scan, then a scatter pass.
+//   large: per-chunk counts + in-chunk ranks (which also preset every slot of the layout to the
+//   padding sentinel), a one-workgroup scan of the offsets, then a scatter pass that writes the
+//   valid slots and the tile -> expert map. Only the offsets go through the single workgroup: its
+//   padding and tile fill took 8 of the 14 us of the 8K-token sort.
 #include "align_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -16,11 +19,18 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_small(const int32_t* id
 }
 
 // Pass 1: per chunk of 1024 slots, the in-chunk stable rank of every slot and the chunk's count
-// per expert (hist[c * E1 + e]).
+// per expert (hist[c * E1 + e]); the workgroups also preset all cap layout slots to the padding
+// sentinel S (weight 0), consecutive threads on consecutive slots. The scatter pass overwrites
+// the valid ones.
 __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* ids, int S, int E1,
-                                                               int32_t* rank_out, int32_t* hist) {
+                                                               int cap, int32_t* rank_out,
+                                                               int32_t* hist, AlignOut o) {
   __shared__ uint16_t wcnt[kAlignWaves][kAlignMaxE1];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int r = blockIdx.x * kAlignThreads + t; r < cap; r += gridDim.x * kAlignThreads) {
+    o.sorted_ids[r] = S;
+    if (o.sorted_w) o.sorted_w[r] = 0.f;
+  }
   for (int e = t; e < E1; e += kAlignThreads)
     for (int w = 0; w < kAlignWaves; ++w) wcnt[w][e] = 0;
   __syncthreads();
@@ -53,6 +63,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
 constexpr int kScanLdsCounts = 28 * 1024;
 __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
                                                               int32_t* __restrict__ start,
+                                                              int32_t* __restrict__ offs,
                                                               int nchunks, int S, int E1, int bm,
                                                               int cap, AlignOut o) {
   __shared__ int cnt[kAlignMaxE1];
@@ -111,7 +122,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
     cnt[x] = s2;
   }
   __syncthreads();
-  align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o, nullptr);
+  align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o, nullptr, false);
+  for (int x = t; x <= E1; x += kAlignThreads) offs[x] = off[x];
   __syncthreads();
   for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
     if (pass == 1 && (P != 1 || ee >= E1)) break;
@@ -124,16 +136,42 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
   }
 }
 
-// Pass 3: sorted_ids[start(chunk, e) + rank] = f (and the slot's weight into sorted_w).
+// Pass 3: sorted_ids[start(chunk, e) + rank] = f (and the slot's weight into sorted_w); the
+// workgroups also write the tile -> expert map, tile b belonging to the expert whose padded range
+// [offs[e], offs[e + 1]) holds row b * bm (a binary search over the offsets in LDS), -1 past the
+// used rows.
 __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const int32_t* ids, int S, int E1,
+                                                                 int bm, int nb,
                                                                  const int32_t* rank_in,
-                                                                 const int32_t* start, AlignOut o) {
-  int f = blockIdx.x * kAlignThreads + threadIdx.x;
-  int e = align_expert_of(ids, f, S, E1);
-  if (e < 0) return;
-  const int pos = start[(size_t)blockIdx.x * E1 + e] + rank_in[f];
-  o.sorted_ids[pos] = f;
-  if (o.sorted_w) o.sorted_w[pos] = o.topk_w[f];
+                                                                 const int32_t* start,
+                                                                 const int32_t* offs, AlignOut o) {
+  __shared__ int off[kAlignMaxE1 + 1];
+  const int t = threadIdx.x;
+  const int f = blockIdx.x * kAlignThreads + t;
+  const int e = align_expert_of(ids, f, S, E1);
+  if (e >= 0) {
+    const int pos = start[(size_t)blockIdx.x * E1 + e] + rank_in[f];
+    o.sorted_ids[pos] = f;
+    if (o.sorted_w) o.sorted_w[pos] = o.topk_w[f];
+  }
+  if (blockIdx.x * kAlignThreads >= nb) return;  // workgroup-uniform: no tiles left for it
+  for (int x = t; x <= E1; x += kAlignThreads) off[x] = offs[x];
+  __syncthreads();
+  const int total = off[E1];
+  for (int b = blockIdx.x * kAlignThreads + t; b < nb; b += gridDim.x * kAlignThreads) {
+    const int r = b * bm;
+    int be = -1;
+    if (r < total) {
+      int lo = 0, hi = E1 - 1;  // largest e with off[e] <= r (empty experts share offsets)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      be = lo;
+    }
+    o.block_expert[b] = be;
+  }
 }
 
 }  // namespace
@@ -149,7 +187,8 @@ size_t align_scratch_bytes(int T, int E, int top_k) {
   size_t nch = (S + kAlignChunk - 1) / kAlignChunk;
   size_t rank = (S * 4 + 255) / 256 * 256;
   size_t hist = (nch * (size_t)(E + 1) * 4 + 255) / 256 * 256;
-  return rank + 2 * hist;  // rank, chunk histograms, chunk starts
+  size_t offs = ((size_t)(E + 2) * 4 + 255) / 256 * 256;
+  return rank + 2 * hist + offs;  // rank, chunk histograms, chunk starts, expert offsets
 }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
@@ -166,11 +205,13 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m
   const size_t hist_bytes = ((size_t)nch * E1 * 4 + 255) / 256 * 256;
   int32_t* hist = (int32_t*)((char*)scratch + ((size_t)S * 4 + 255) / 256 * 256);
   int32_t* start = (int32_t*)((char*)hist + hist_bytes);
-  hipLaunchKernelGGL(k_align_count, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank, hist);
-  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, start, nch, S, E1,
-                     block_m, cap, o);
-  hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, rank,
-                     start, o);
+  int32_t* offs = (int32_t*)((char*)start + hist_bytes);
+  hipLaunchKernelGGL(k_align_count, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, cap, rank,
+                     hist, o);
+  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, start, offs, nch, S,
+                     E1, block_m, cap, o);
+  hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, block_m,
+                     cap / block_m, rank, start, offs, o);
   return hipGetLastError();
 }
 

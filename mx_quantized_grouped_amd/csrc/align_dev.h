@@ -92,10 +92,12 @@ __device__ __forceinline__ int align_expert_of(const int32_t* ids, int f, int S,
 
 // From per-expert counts cnt[0..E1): padded offsets off[0..E1], the touched-expert list and all
 // layout outputs except the scatter of valid slots. Called by the whole 1024-thread workgroup.
-// tile_e: LDS room for kTileMapMax tile -> expert entries, or null.
+// tile_e: LDS room for kTileMapMax tile -> expert entries, or null. With fill false, the padding
+// slots and the tile -> expert map are left to the caller (the multi-workgroup sort writes them
+// from its parallel passes).
 inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1, int S, int bm,
                                                 int cap, int* s_wave, const AlignOut& o,
-                                                int16_t* tile_e) {
+                                                int16_t* tile_e, bool fill = true) {
   const int t = threadIdx.x;
   const int e0 = 2 * t, e1 = 2 * t + 1;
   int c0 = e0 < E1 ? cnt[e0] : 0, c1 = e1 < E1 ? cnt[e1] : 0;
@@ -118,6 +120,7 @@ inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1
   __syncthreads();
   if (o.expert_off)
     for (int e = t; e <= E1; e += kAlignThreads) o.expert_off[e] = off[e];
+  if (!fill) return;
   const int nb = cap / bm;
   if (tile_e && nb <= kTileMapMax && cap <= kParallelFillMax) {
     // Small layout: the tile -> expert map goes to LDS, then every tile and slot is visited by
