@@ -163,8 +163,10 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
 
 /* Host: where forward keeps an intermediate inside its workspace, for inspection after the call
  * (routing table, sorted layout, quantised activations). which: 0 topk_ids, 1 topk_w,
- * 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off. Returns the byte offset and writes
- * the byte size to *bytes; the tile height forward used is written to *block_m. Returns
+ * 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off, 6 activation codes [T, H] (E4M3,
+ * MX weights only; size 0 otherwise), 7 activation scale bytes [T, srs] with srs = H/32 rounded up
+ * to a multiple of 16 (K-block order, padding bytes unspecified). Returns the byte offset and
+ * writes the byte size to *bytes; the tile height forward used is written to *block_m. Returns
  * (size_t)-1 for an invalid request. */
 size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int which,
                             size_t* bytes, int* block_m);

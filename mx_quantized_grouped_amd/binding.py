@@ -18,7 +18,8 @@ MXMOE_OK, MXMOE_EINVAL, MXMOE_EUNSUPPORTED, MXMOE_EWORKSPACE, MXMOE_EHIP = 0, -1
 MXMOE_BF16, MXMOE_F32, MXMOE_MXFP8_E4M3, MXMOE_MXFP4_E2M1 = 0, 1, 2, 3
 MXMOE_LAUNCH_AUTO, MXMOE_LAUNCH_SMALL_M, MXMOE_LAUNCH_LARGE_M = 0, 1, 2
 MXMOE_COMBINE_AUTO, MXMOE_COMBINE_SLOTS, MXMOE_COMBINE_ATOMIC, MXMOE_COMBINE_SLOTS_BF16 = 0, 1, 2, 3
-VIEW_TOPK_IDS, VIEW_TOPK_W, VIEW_SORTED_IDS, VIEW_BLOCK_EXPERT, VIEW_NUM_POST_PAD, VIEW_EXPERT_OFF = range(6)
+(VIEW_TOPK_IDS, VIEW_TOPK_W, VIEW_SORTED_IDS, VIEW_BLOCK_EXPERT, VIEW_NUM_POST_PAD, VIEW_EXPERT_OFF,
+ VIEW_XQ, VIEW_XS) = range(8)
 
 FMT_BY_NAME = {"bf16": MXMOE_BF16, "f32": MXMOE_F32, "mxfp8": MXMOE_MXFP8_E4M3,
                "mxfp4": MXMOE_MXFP4_E2M1}

@@ -242,10 +242,12 @@ size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int 
                             size_t* bytes, int* block_m) {
   Plan p;
   if (make_plan(s, opt, &p)) return (size_t)-1;
-  static const int segs[6] = {SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF};
-  if (which < 0 || which > 5) return (size_t)-1;
-  size_t sz[6] = {(size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4,
-                  (size_t)(p.cap / p.bm) * 4, 4, (size_t)(p.E1 + 1) * 4};
+  static const int segs[8] = {SEG_IDS,      SEG_W,      SEG_SORTED, SEG_BLOCKEXP,
+                              SEG_COUNTERS, SEG_EXPOFF, SEG_XQ,     SEG_XS};
+  if (which < 0 || which > 7) return (size_t)-1;
+  size_t sz[8] = {(size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4,
+                  (size_t)(p.cap / p.bm) * 4, 4, (size_t)(p.E1 + 1) * 4,
+                  p.mx ? (size_t)p.T * p.H : 0, p.mx ? (size_t)p.T * p.srs_H : 0};
   if (bytes) *bytes = sz[which];
   if (block_m) *block_m = p.bm;
   return p.off[segs[which]];

@@ -32,18 +32,12 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
     align_small_body(ids_lds, a.T * (a.top_k + 1), a.E + 1, a.block_m, a.cap, a.out, sm);
     return;
   }
-  const size_t blk = (size_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
+  const size_t g = (size_t)(blockIdx.x - 1) * kThreads + threadIdx.x;
+  const size_t blk = g >> 2;  // four lanes per block
   const int nbk = a.H / 32;
   if (blk >= (size_t)a.T * nbk) return;
   const size_t t = blk / nbk;
-  const int kb = (int)(blk - t * nbk);
-  if (a.xq) {
-    quant_act_block(a.x, t, kb, a.H, a.xq, a.xs, a.srs, a.zero_out);
-  } else if (a.zero_out) {
-    v4f* z = (v4f*)(a.zero_out + t * a.H + (size_t)kb * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
+  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.zero_out);
 }
 
 // Larger batches: workgroups [0, n_route) route 16 tokens each; the rest quantise / clear.
@@ -58,18 +52,12 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_
                             nullptr);
     return;
   }
-  const size_t blk = (size_t)(blockIdx.x - n_route) * kThreads + threadIdx.x;
+  const size_t g = (size_t)(blockIdx.x - n_route) * kThreads + threadIdx.x;
+  const size_t blk = g >> 2;  // four lanes per block
   const int nbk = a.H / 32;
   if (blk >= (size_t)a.T * nbk) return;
   const size_t t = blk / nbk;
-  const int kb = (int)(blk - t * nbk);
-  if (a.xq) {
-    quant_act_block(a.x, t, kb, a.H, a.xq, a.xs, a.srs, a.zero_out);
-  } else if (a.zero_out) {
-    v4f* z = (v4f*)(a.zero_out + t * a.H + (size_t)kb * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
+  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.zero_out);
 }
 
 }  // namespace
@@ -78,7 +66,7 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
                            hipStream_t st) {
   const int S = a.T * (a.top_k + 1);
   const bool work = a.xq || a.zero_out;
-  const int nq = work ? (int)(((size_t)a.T * (a.H / 32) + kThreads - 1) / kThreads) : 0;
+  const int nq = work ? (int)(((size_t)a.T * (a.H / 32) * 4 + kThreads - 1) / kThreads) : 0;
   // One launch while one workgroup's 16 waves route every token two at most each: a wave routes a
   // token in about 1.7 us, so at 32 tokens the fused kernel (about 11.4 us) still beats a routing
   // launch plus a sort launch (about 12.9 us with the gap between them); beyond that, routing

@@ -45,10 +45,11 @@ __global__ __launch_bounds__(256) void k_quant_canonical(const void* src, int ro
 __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* x, int T, int H, uint8_t* xq,
                                                    uint8_t* xs, int srs, float* zero_out) {
   const int nbk = H / 32;
-  size_t blk = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t blk = g >> 2;  // four lanes per block
   if (blk >= (size_t)T * nbk) return;
-  size_t t = blk / nbk;
-  quant_act_block(x, t, (int)(blk - t * nbk), H, xq, xs, srs, zero_out);
+  const size_t t = blk / nbk;
+  quant_act_part(x, t, (int)(blk - t * nbk), (int)(g & 3), H, xq, xs, srs, zero_out);
 }
 
 __global__ __launch_bounds__(256) void k_zero_f32(float* p, size_t n) {
@@ -77,8 +78,8 @@ hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* xq, uin
                                int srs, float* zero_out, hipStream_t st) {
   size_t nblk = (size_t)T * (H / 32);
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, x, T, H,
-                     xq, xs, srs, zero_out);
+  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((4 * nblk + 255) / 256)), dim3(256), 0, st, x,
+                     T, H, xq, xs, srs, zero_out);
   return hipGetLastError();
 }
 

@@ -134,5 +134,11 @@ def test_workspace_view(L):
     off, nb, bm = B.mxmoe_workspace_view(s, B.Options(2, 2, 128, 0), B.VIEW_SORTED_IDS)
     assert bm == 128 and nb == 4 * L.mxmoe_align_capacity(32, 128, 8, 128)
     assert off % 256 == 0
+    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_XQ)
+    assert nb == 32 * 3072 and off % 256 == 0
+    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_XS)
+    assert nb == 32 * 96                                 # 3072 / 32 scale bytes, already 16-aligned
+    sb = B.Shape.of(16, 256, 8, 2, 128, "bf16")
+    assert B.mxmoe_workspace_view(sb, None, B.VIEW_XQ)[1] == 0   # bf16 weights: no activation codes
     with pytest.raises(B.MxMoeError):
         B.mxmoe_workspace_view(s, None, 9)

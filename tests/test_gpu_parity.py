@@ -230,6 +230,49 @@ def test_forward_parity_launchers(name, launcher, combine):
     _check_forward(name, B.Options(launcher, combine, 0, 0))
 
 
+def _check_act_codes(shape, ws, options, xbits):
+    """The activation codes and scales forward left in its workspace against the oracle's MX rule."""
+    T, H = xbits.shape
+    xq, _ = _view(ws, shape, options, B.VIEW_XQ, torch.uint8)
+    xs, _ = _view(ws, shape, options, B.VIEW_XS, torch.uint8)
+    rc, rs = mx.quantize(f64(xbits), "e4m3")
+    assert np.array_equal(xq.reshape(T, H), rc)
+    assert np.array_equal(xs.reshape(T, -1)[:, :H // 32], rs)
+
+
+@pytest.mark.parametrize("name", ["decode_mxfp8", "wide512_mxfp4_T6", "prefill_mxfp8"])
+def test_forward_activation_codes_bit_exact(name):
+    # the in-forward quantiser (one-launch and split prologues) against the oracle, every code
+    _say("activation codes", name)
+    w, xb, _ = inputs(name)
+    _, shape, _, ws = _run_forward(name, None)
+    _check_act_codes(shape, ws, None, xb)
+
+
+def test_forward_activation_codes_exhaustive_bf16():
+    # every finite bf16 value once, shuffled into a 32 x 2048 activation matrix
+    _say("activation codes exhaustive")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(workloads.f32_from_bf16_bits(bits))]
+    bits = np.random.default_rng(3).permutation(bits)
+    T, H = 32, 2048
+    xb = np.zeros(T * H, dtype=np.uint16)
+    xb[:bits.size] = bits
+    xb = xb.reshape(T, H)
+    wl = workloads.Workload("act_exhaustive", T, H, 4, 2, 128, "mxfp8", "mxfp8", False, 7)
+    from mx_quantized_grouped_amd.weights import ExpertLoader
+    shape = shape_of(wl)
+    loader = ExpertLoader(shape, DEV)
+    for e in range(wl.E + 1):
+        loader.add_expert(e, *workloads.draw_expert(wl, e))
+    packed = loader.finish()
+    lb = workloads.draw_logits(wl)
+    ws = torch.empty(B.mxmoe_workspace_bytes(shape, None), dtype=torch.uint8, device=DEV)
+    B.mxmoe_forward(shape, bf16_tensor(xb), bf16_tensor(lb), packed, workspace=ws)
+    torch.cuda.synchronize()
+    _check_act_codes(shape, ws, None, xb)
+
+
 @pytest.mark.parametrize("bm", [16, 32, 128, 256])
 def test_forward_block_m(bm):
     _say("forward block_m", bm)
