@@ -48,13 +48,6 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
   return se < -127 ? -127 : (se > 127 ? 127 : se);
 }
 
-// E4M3 magnitude code of a in [0, 448]: round to nearest, ties to even.
-__device__ __forceinline__ uint32_t e4m3_mag(float a) {
-  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal grid m * 2^-9
-  uint32_t u = __float_as_uint(a);
-  u += 0x7FFFFu + ((u >> 20) & 1u);                                  // keep 3 mantissa bits
-  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);               // rebias 127 -> 7
-}
 // E2M1 magnitude code of a in [0, 6].
 __device__ __forceinline__ uint32_t e2m1_mag(float a) {
   if (a < 1.0f) return (uint32_t)__builtin_rintf(a * 2.0f);          // 0, 0.5, 1.0 (code 2)
@@ -62,12 +55,26 @@ __device__ __forceinline__ uint32_t e2m1_mag(float a) {
   u += 0x1FFFFFu + ((u >> 22) & 1u);                                 // keep 1 mantissa bit
   return (((u >> 23) - 126u) << 1) | ((u >> 22) & 1u);               // rebias 127 -> 1
 }
-// Element code of x in a block with shared exponent se (sign kept, saturating).
-__device__ __forceinline__ uint32_t e4m3_code(float x, int se) {
-  float v = ldexpf(x, -se);
-  uint32_t m = e4m3_mag(fminf(fabsf(v), 448.0f));
-  return m | ((__float_as_uint(v) >> 24) & 0x80u);
+// E4M3 codes of two elements of a block with shared exponent se, element a in the low byte: the
+// nearest code of x / 2^se, ties to even, saturating at 448, sign kept. x / 2^se is exact (a
+// power-of-two scaling of a finite value) and clamped to +-448, then the hardware's packed E4M3
+// conversion rounds it to nearest even. The device quantisers' codes are checked bit-exactly
+// against the reference rule on every finite bf16 value and on fp32 blocks with exact ties.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b, int se) {
+  const float ca = fminf(fmaxf(ldexpf(a, -se), -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(ldexpf(b, -se), -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
 }
+// Four codes packed little-endian into a dword.
+__device__ __forceinline__ uint32_t e4m3_quad(float a, float b, float c, float d, int se) {
+  const float ca = fminf(fmaxf(ldexpf(a, -se), -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(ldexpf(b, -se), -448.0f), 448.0f);
+  const float cc = fminf(fmaxf(ldexpf(c, -se), -448.0f), 448.0f);
+  const float cd = fminf(fmaxf(ldexpf(d, -se), -448.0f), 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, lo, true);
+}
+// E2M1 element code of x in a block with shared exponent se (sign kept, saturating at 6).
 __device__ __forceinline__ uint32_t e2m1_code(float x, int se) {
   float v = ldexpf(x, -se);
   uint32_t m = e2m1_mag(fminf(fabsf(v), 6.0f));

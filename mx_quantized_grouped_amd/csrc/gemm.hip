@@ -222,8 +222,9 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
         int se = mx_shared_exp<8>(m);
         if (rr < r1) {
           uint8_t* hr = p.h + (size_t)rr * p.h_stride + ic0;
-          hr[n] = (uint8_t)e4m3_code(a0, se);
-          hr[16 + n] = (uint8_t)e4m3_code(a1, se);
+          const uint32_t c2 = e4m3_pair(a0, a1, se);
+          hr[n] = (uint8_t)c2;
+          hr[16 + n] = (uint8_t)(c2 >> 8);
           if (n == 0) p.hs[(size_t)rr * p.h_srs + chunk] = (uint8_t)(se + 127);
         }
       } else if (rr < r1) {
@@ -472,8 +473,9 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
       const float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
       const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
       const int se = mx_shared_exp<8>(m);
-      codes[row * kPitch + 32 * wave + n] = (uint8_t)e4m3_code(a0, se);
-      codes[row * kPitch + 32 * wave + 16 + n] = (uint8_t)e4m3_code(a1, se);
+      const uint32_t c2 = e4m3_pair(a0, a1, se);
+      codes[row * kPitch + 32 * wave + n] = (uint8_t)c2;
+      codes[row * kPitch + 32 * wave + 16 + n] = (uint8_t)(c2 >> 8);
       if (n == 0) ((uint8_t*)scales)[4 * row + wave] = (uint8_t)(se + 127);
     }
   }

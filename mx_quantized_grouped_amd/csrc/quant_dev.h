@@ -41,8 +41,7 @@ __device__ __forceinline__ float amax32(const float* v) {
 __device__ __forceinline__ void encode_fp8_32(const float* v, int se, uint32_t* out) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    out[i] = e4m3_code(v[4 * i], se) | (e4m3_code(v[4 * i + 1], se) << 8) |
-             (e4m3_code(v[4 * i + 2], se) << 16) | (e4m3_code(v[4 * i + 3], se) << 24);
+    out[i] = e4m3_quad(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], se);
 }
 // 32 E2M1 codes, element 2i in the low nibble of byte i, packed into 4 dwords.
 __device__ __forceinline__ void encode_fp4_32(const float* v, int se, uint32_t* out) {
@@ -83,16 +82,8 @@ __device__ __forceinline__ void quant_act_part(const uint16_t* x, size_t t, int 
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x4E, 0xF, 0xF, false)));
     const int se = mx_shared_exp<8>(m);
     if (part == 0) xs[t * srs + kb] = (uint8_t)(se + 127);
-    // x / 2^se clamped to +-448 (exact: a power-of-two scaling of a finite value), then the
-    // hardware's packed conversion to E4M3, which rounds to nearest even like e4m3_code
-    float c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(ldexpf(v[i], -se), -448.0f), 448.0f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
-    *(uint2*)(xq + off) = uint2{(uint32_t)lo, (uint32_t)hi};
+    *(uint2*)(xq + off) = uint2{e4m3_quad(v[0], v[1], v[2], v[3], se),
+                                e4m3_quad(v[4], v[5], v[6], v[7], se)};
   }
   if (zero_out) {
     v4f* z = (v4f*)(zero_out + off);
