@@ -490,6 +490,13 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
     *(uint32_t*)(p.hs + (size_t)(r0 + tid) * p.h_srs + 4 * chunk) = scales[tid];
 }
 
+// Barrier for LDS reuse only: waits for this wave's LDS operations, then for the workgroup. The
+// release fence of __syncthreads also waits for every global store the wave has outstanding,
+// which put the write latency of each staged pass of the down epilogue on the critical path.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // down epilogue with bf16 slot rows: the tile's 128 x 256 bf16 products w(row) * d(row) are staged
 // in LDS (row pitch 512 + 32 bytes, so the four rows one store instruction touches fall in
 // different banks), then each slot row's 512-byte segment goes out as 16-byte stores (32 lanes per
@@ -510,7 +517,7 @@ __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4
   uint16_t* out16 = (uint16_t*)p.out32;
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
-    if (pass) __syncthreads();  // the previous pass's rows have been copied out
+    if (pass) lds_barrier();  // the previous pass's rows have been read back (stores may fly)
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) {
       const int mt = pass * kGroups + q;
@@ -523,7 +530,7 @@ __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4
           orow[16 * f] = (uint16_t)f32_to_bf16_bits(wt[i] * acc[mt][f][i]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll 4
     for (int j = 0; j < kRows * 32 / 256; ++j) {
       const int c = tid + 256 * j, lrow = c >> 5, unit = c & 31;
@@ -651,7 +658,10 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
     step(std::integral_constant<int, 0>{}, ks);
     step(std::integral_constant<int, 1>{}, ks + 1);
   }
-  if (ks < nks) compute(0, bs[0], 0, MT);  // odd step count: the last step alone (nothing to load)
+  if (ks < nks) {  // odd step count: the last step alone (nothing to load)
+    compute(0, bs[0], 0, MT);
+    lds_barrier();  // every wave's reads of stage 0 are done before the epilogue reuses it
+  }
   if constexpr (GATE_UP) {
     epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds);
   } else {
