@@ -8,7 +8,8 @@ it shares no code with the GPU path. Each function states the passage it follows
   [K3]  "Tối ưu hiệu năng Kimi K3 trong vLLM: Hành trình đạt thông lượng gấp 2,8 lần"
   [L3]  "Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell"
 
-The block, per token t with bf16 activations x[t] and bf16 router logits l[t]:
+The block, per token t with bf16 activations x[t] and bf16 router logits l[t] (or logits from the
+gate in front of it, step 0: l = x . W_g^T, [L3] "Sửa thước đo trước khi sửa máy"):
   1. route  : top-k routed experts by logit (ties to the lower index), softmax weights over the k
               selected, and the shared expert appended as slot k with weight 1   ([M3] shared-expert
               passage, Fig. 4: the shared expert is a table entry every token selects).
@@ -32,6 +33,22 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import mx
+
+
+# ---------------------------------------------------------------- 0. gate (in front of route)
+def gate_logits(x: np.ndarray, w_gate: np.ndarray) -> np.ndarray:
+    """Router logits l[t, e] = sum_h x[t, h] * w_gate[e, h] in fp64.
+
+    x: [T, H] and w_gate: [E, H] (bf16 values held in fp64). [L3] "Sửa thước đo trước khi sửa
+    máy" names a bf16 gate in front of the router (a 2.6 MB gate-weight kernel): reading, the
+    gate's operands are bf16 and its products are summed in at least fp32, so the exact sum of
+    the bf16 products is the reference and a device result differs from it only by accumulation
+    rounding. The definition is the matrix product itself."""
+    x = np.asarray(x, dtype=np.float64)
+    w_gate = np.asarray(w_gate, dtype=np.float64)
+    if x.ndim != 2 or w_gate.ndim != 2 or x.shape[1] != w_gate.shape[1]:
+        raise ValueError("need x [T, H] and w_gate [E, H]")
+    return x @ w_gate.T
 
 
 # ---------------------------------------------------------------- 1. route

@@ -16,6 +16,32 @@ from oracle import moe, mx
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+# ------------------------------------------------------------------------------------ gate
+def test_gate_hand_example():
+    # 2 tokens, 3 experts, H = 2: every logit worked by hand
+    x = np.array([[1.0, 2.0], [-0.5, 4.0]])
+    w = np.array([[1.0, 0.0], [0.25, -1.0], [3.0, 0.5]])
+    assert moe.gate_logits(x, w).tolist() == [[1.0, -1.75, 4.0], [-0.5, -4.125, 0.5]]
+
+
+def test_gate_matches_loops_and_one_hot_rows():
+    rng = np.random.default_rng(5)
+    x = workloads.f32_from_bf16_bits(workloads.bf16_bits_from_f32(
+        rng.standard_normal((5, 64)).astype(np.float32))).astype(np.float64)
+    w = workloads.f32_from_bf16_bits(workloads.bf16_bits_from_f32(
+        (0.02 * rng.standard_normal((7, 64))).astype(np.float32))).astype(np.float64)
+    ref = moe.gate_logits(x, w)
+    for t in range(5):                       # brute force: one exact sum per logit
+        for e in range(7):
+            assert ref[t, e] == pytest.approx(math.fsum(x[t, h] * w[e, h] for h in range(64)),
+                                              rel=1e-13, abs=1e-15)
+    onehot = np.zeros((3, 64))
+    onehot[0, 5] = onehot[1, 0] = onehot[2, 63] = 1.0   # expert e reads one column of x
+    assert np.array_equal(moe.gate_logits(x, onehot), x[:, [5, 0, 63]])
+    with pytest.raises(ValueError):
+        moe.gate_logits(x, w[:, :32])
+
+
 # ------------------------------------------------------------------------------------ route
 def test_route_hand_examples():
     ids, w = moe.route(np.array([[1.0, 3.0, 3.0, 2.0]]), 2)
