@@ -11,7 +11,9 @@ Prints one JSON line. `value` is the headline workload's algorithmic HBM through
 decode M; per-workload TFLOP/s, GB/s and roofline fractions (decode and prefill M) are in
 `workloads`. `roofline` is for the dominant kernel (gate_up), timed with HIP events that the
 library records on its own stream at stage boundaries. `cpu_baseline` is the fp64 CPU oracle on a
-bounded sample of the headline workload (host cores of the same machine)."""
+bounded sample of the headline workload (host cores of the same machine). `gate` times the router
+gate in front of the block (mxmoe_gate, x . W_g^T to fp32 logits) on each workload's shapes, its
+weights in cache between back-to-back calls."""
 from __future__ import annotations
 
 import argparse
@@ -176,6 +178,31 @@ def measure(name, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
+def measure_gate(name, steps=100):
+    """Router gate (mxmoe_gate, fp32 logits) on the workload's x [T, H] and a seeded bf16 gate
+    [E, H], launched back to back (its weights stay in cache between calls)."""
+    import torch
+    import workloads
+    from mx_quantized_grouped_amd import binding as B
+    w = workloads.get(name)
+    x = torch.from_numpy(workloads.draw_x(w).view(np.int16)).to("cuda").view(torch.bfloat16)
+    gw = torch.from_numpy(workloads.draw_gate(w).view(np.int16)).to("cuda").view(torch.bfloat16)
+    out = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    for _ in range(5):
+        B.mxmoe_gate(x, gw, logits=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        B.mxmoe_gate(x, gw, logits=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = 2 * w.T * w.H + 2 * w.E * w.H + 4 * w.T * w.E
+    return {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "TFLOPs": 2.0 * w.T * w.H * w.E / (us * 1e-6) / 1e12, "weights": "in cache"}
+
+
 def cpu_baseline(g, n_tokens, min_seconds=10.0):
     """The fp64 oracle on a bounded sample: n_tokens tokens of the same workload. Weight codes are
     produced before the timed region (load-time work); the timed region is the block itself:
@@ -288,6 +315,7 @@ def main():
         others[n] = r
         del gx
         torch.cuda.empty_cache()
+    gate = {n: measure_gate(n) for n in [args.workload] + extra}
     rl = dict(head["roofline"])
     rl["traffic"] = traffic_record(args.workload,
                                    os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"))
@@ -303,7 +331,7 @@ def main():
                    "parallelism": "single GPU (one TP share, all experts resident)"},
         "tflops": head["TFLOPs"], "hbm_frac": head["hbm_frac"], "mfma_frac": head["mfma_frac"],
         "touched_experts": head["touched_experts"], "stage_ms": head["stage_ms"],
-        "roofline": rl, "cpu_baseline": base,
+        "roofline": rl, "cpu_baseline": base, "gate": gate,
         "workloads": {n: {k: v for k, v in r.items() if k not in ("T", "H", "E", "top_k",
                                                                   "shared_experts")}
                       for n, r in others.items()},

@@ -90,6 +90,20 @@ typedef struct {
 /* Host: static description of a status code. Never NULL. */
 const char* mxmoe_status_string(int status);
 
+/* ---------------------------------------------------------------------------------- gate
+ * Router gate, the step in front of route: logits[t, e] = sum_h x[t, h] * w_gate[e, h] with bf16
+ * operands and fp32 accumulation (the bf16 gate of "Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên
+ * 54% trên 4 GPU Blackwell", section "Sửa thước đo trước khi sửa máy").
+ * x      [T, H] bf16 row-major, 16-byte aligned; H % 32 == 0.
+ * w_gate [E, H] bf16 row-major, 16-byte aligned; 1 <= E <= the routed-expert limit.
+ * logits [T, E] row-major, written as fp32 (logits_dtype MXMOE_F32) or bf16 rounded to nearest
+ *        even (MXMOE_BF16); its dtype is what mxmoe_route / mxmoe_forward then take.
+ * The sum over h is split and combined in a fixed order: results are reproducible run to run.
+ * T == 0 is a no-op. Bad sizes, null pointers or misalignment return MXMOE_EINVAL before any
+ * HIP call; the caller owns every buffer. */
+int mxmoe_gate(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
+               void* logits, void* stream);
+
 /* --------------------------------------------------------------------------------- route
  * Top-k routing with the fixed lowest-index tie-break.
  * logits   [T, E] row-major, bf16 or fp32 (logits_dtype).

@@ -25,7 +25,7 @@ FMT_BY_NAME = {"bf16": MXMOE_BF16, "f32": MXMOE_F32, "mxfp8": MXMOE_MXFP8_E4M3,
                "mxfp4": MXMOE_MXFP4_E2M1}
 
 EXPORTS = [
-    "mxmoe_status_string", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
+    "mxmoe_status_string", "mxmoe_gate", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
     "mxmoe_align", "mxmoe_quantize", "mxmoe_prepacked_bytes", "mxmoe_prepack",
     "mxmoe_workspace_bytes", "mxmoe_workspace_bytes_ex", "mxmoe_forward", "mxmoe_forward_ex",
     "mxmoe_workspace_view",
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
     sp, op = ctypes.POINTER(Shape), ctypes.POINTER(Options)
     sig = {
         "mxmoe_status_string": (ctypes.c_char_p, [i32]),
+        "mxmoe_gate": (i32, [vp, vp, i32, i32, i32, i32, vp, vp]),
         "mxmoe_route": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
         "mxmoe_align_capacity": (sz, [i32, i32, i32, i32]),
         "mxmoe_align_workspace_bytes": (sz, [i32, i32, i32, i32]),
@@ -129,6 +130,19 @@ def _dev(t):
 # ----------------------------------------------------------------------------- entry points
 def mxmoe_status_string(status: int) -> str:
     return status_string(status)
+
+
+def mxmoe_gate(x: torch.Tensor, w_gate: torch.Tensor, out_dtype=torch.float32, logits=None,
+               stream=None):
+    """Router logits x . w_gate^T (bf16 operands, fp32 sums) as a [T, E] fp32 or bf16 tensor."""
+    T, H = x.shape
+    E = w_gate.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=out_dtype, device=_dev(x))
+    ld = MXMOE_F32 if logits.dtype == torch.float32 else MXMOE_BF16
+    _check(lib().mxmoe_gate(_ptr(x), _ptr(w_gate), T, H, E, ld, _ptr(logits), _stream(stream)),
+           "mxmoe_gate")
+    return logits
 
 
 def mxmoe_route(logits: torch.Tensor, top_k: int, topk_ids=None, topk_w=None, stream=None):

@@ -144,6 +144,19 @@ const char* mxmoe_status_string(int status) {
   }
 }
 
+int mxmoe_gate(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
+               void* logits, void* stream) {
+  if (T < 0 || H <= 0 || H % 32 || E < 1 || E > kMaxExperts) return MXMOE_EINVAL;
+  if ((size_t)64 * H * 2 > 0x7FFFFFFFu) return MXMOE_EINVAL;  // tile offsets stay below 2^31
+  if (logits_dtype != MXMOE_BF16 && logits_dtype != MXMOE_F32) return MXMOE_EINVAL;
+  if (T == 0) return MXMOE_OK;
+  if (!x || !w_gate || !logits) return MXMOE_EINVAL;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(logits, logits_dtype == MXMOE_F32 ? 4 : 2))
+    return MXMOE_EINVAL;
+  return hip_status(launch_gate((const uint16_t*)x, (const uint16_t*)w_gate, T, H, E,
+                                logits_dtype == MXMOE_F32, logits, (hipStream_t)stream));
+}
+
 int mxmoe_route(const void* logits, int T, int E, int top_k, int logits_dtype, int32_t* topk_ids,
                 float* topk_w, void* stream) {
   int rc = check_route_args(T, E, top_k);

@@ -12,6 +12,10 @@ constexpr int kAlignSmallMaxSlots = 4096;
 constexpr int kAlignChunk = 1024; // slots per workgroup in the multi-workgroup sort
 
 // route.hip
+// gate.hip
+hipError_t launch_gate(const uint16_t* x, const uint16_t* w_gate, int T, int H, int E, bool out_f32,
+                       void* logits, hipStream_t st);
+
 hipError_t launch_route(const void* logits, bool logits_f32, int T, int E, int top_k,
                         int32_t* ids, float* w, hipStream_t st);
 

@@ -52,6 +52,22 @@ def test_route_validation(L):
              None) == B.MXMOE_EINVAL                                     # misaligned fp32
 
 
+def test_gate_validation(L):
+    gt = L.mxmoe_gate
+    p = ctypes.c_void_p(4096)
+    assert gt(p, p, 4, 100, 8, 1, p, None) == B.MXMOE_EINVAL                # H % 32 != 0
+    assert gt(p, p, 4, 0, 8, 1, p, None) == B.MXMOE_EINVAL                  # H = 0
+    assert gt(p, p, 4, 128, 0, 1, p, None) == B.MXMOE_EINVAL                # E < 1
+    assert gt(p, p, 4, 128, 5000, 1, p, None) == B.MXMOE_EINVAL             # E too large
+    assert gt(p, p, -1, 128, 8, 1, p, None) == B.MXMOE_EINVAL               # T < 0
+    assert gt(p, p, 4, 128, 8, 7, p, None) == B.MXMOE_EINVAL                # bad dtype
+    assert gt(None, p, 4, 128, 8, 1, p, None) == B.MXMOE_EINVAL             # null x
+    assert gt(p, p, 4, 128, 8, 1, None, None) == B.MXMOE_EINVAL             # null logits
+    assert gt(ctypes.c_void_p(4104), p, 4, 128, 8, 1, p, None) == B.MXMOE_EINVAL  # x misaligned
+    assert gt(p, p, 4, 128, 8, 1, ctypes.c_void_p(4098), None) == B.MXMOE_EINVAL  # fp32 misaligned
+    assert gt(None, None, 0, 128, 8, 1, None, None) == B.MXMOE_OK           # T = 0 no-op
+
+
 def test_align_validation_and_capacity(L):
     assert L.mxmoe_align_capacity(3, 2, 1, 2) == 0                       # block_m not allowed
     # S = 6 slots, at most min(E+1, S) = 3 touched experts: 6 + 3*15 = 51, rounded up to 16 -> 64

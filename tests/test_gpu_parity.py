@@ -97,6 +97,60 @@ def test_weight_quantisation_matches_oracle(name):
             assert np.array_equal(dev_c.cpu().numpy(), rc), (name, e)
 
 
+# ------------------------------------------------------------------------------- gate
+def _gate_bound(xb, gb):
+    """fp32 accumulation bound for the gate: |err| <= H * 2^-24 * sum_h |x_h w_h| per logit
+    (recursive summation of H exact bf16 products, each partial sum rounded once; the products of
+    two bf16 values are exact in fp32)."""
+    H = xb.shape[1]
+    return H * 2.0 ** -24 * (np.abs(f64(xb)) @ np.abs(f64(gb)).T)
+
+
+@pytest.mark.parametrize("T,H,E", [(32, 3072, 128), (8192, 3072, 128), (6, 2048, 512),
+                                   (1, 2048, 512), (37, 96, 70), (100, 64, 1), (65, 128, 130)])
+def test_gate_parity(T, H, E):
+    _say("gate", T, H, E)
+    wl = workloads.Workload(f"gate_{T}_{H}_{E}", T, H, E, 1, 128, "mxfp8", "mxfp8", False, 9)
+    xb, gb = workloads.draw_x(wl), workloads.draw_gate(wl)
+    ref = moe.gate_logits(f64(xb), f64(gb))
+    bound = _gate_bound(xb, gb)
+    x, g = bf16_tensor(xb), bf16_tensor(gb)
+    l32 = B.mxmoe_gate(x, g)
+    l16 = B.mxmoe_gate(x, g, out_dtype=torch.bfloat16)
+    again = B.mxmoe_gate(x, g)
+    torch.cuda.synchronize()
+    a = l32.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(a - ref) <= bound), np.max(np.abs(a - ref) - bound)
+    assert torch.equal(l32, again)                      # fixed-order sums: reproducible
+    b = l16.float().cpu().numpy().astype(np.float64)   # one more rounding, to bf16
+    assert np.all(np.abs(b - ref) <= bound + 2.0 ** -8 * np.abs(ref))
+
+
+def test_gate_then_route_and_forward():
+    # gate -> route inside forward: the routing of the GPU's logits is the oracle's routing of
+    # those same logits (bit-exact), and the block output is within tolerance of the oracle's
+    _say("gate -> forward")
+    name = "decode_mxfp8"
+    w, xb, _ = inputs(name)
+    _, packed = packed_weights(name)
+    gb = workloads.draw_gate(w)
+    x = bf16_tensor(xb)
+    logits = B.mxmoe_gate(x, bf16_tensor(gb))
+    shape = shape_of(w, "f32")
+    ws = torch.empty(B.mxmoe_workspace_bytes(shape, None), dtype=torch.uint8, device=DEV)
+    y = B.mxmoe_forward(shape, x, logits, packed, workspace=ws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(lg - moe.gate_logits(f64(xb), f64(gb))) <= _gate_bound(xb, gb))
+    ids, _ = _view(ws, shape, None, B.VIEW_TOPK_IDS)
+    rid, _ = moe.route(lg, w.top_k)
+    assert np.array_equal(ids.reshape(w.T, w.top_k + 1), rid)
+    toks = np.arange(0, w.T, 4)
+    ref = moe.moe_block(f64(xb), lg, oracle_weights(w), w.top_k, w.act_fmt, tokens=toks)
+    st = moe.parity_stats(y.float().cpu().numpy().astype(np.float64)[toks], ref.y[toks])
+    assert tolerance_ok(st), st
+
+
 # ------------------------------------------------------------------------------- route
 def _check_route(lg64, dev_logits, k):
     ids, wts = B.mxmoe_route(dev_logits, k)

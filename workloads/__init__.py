@@ -17,6 +17,8 @@ Draw recipe (per workload, seed s):
   * logits : [T, E]  N(0, 1) in fp32, plus (for Zipf workloads) a per-expert bias
              b_e = -1.1 * ln(e + 1) added in fp32, then rounded to bf16. Softmax routing then picks
              expert e with odds proportional to (e + 1)^-1.1, i.e. Zipf(s = 1.1) popularity.
+  * gate   : [E, H]  N(0, 1/H) in fp32, rounded to bf16 (for the router gate in front of the
+             routing step; logits = x . gate^T are then about N(0, 1)).
   * weights: for each expert e in 0..E (E is the shared expert) an independent stream gives
              W13 [2I, H] (gate rows 0..I-1, then up rows I..2I-1) and then W2 [H, I],
              N(0, 0.02) in fp32 (standard normal times 0.02 in fp32). bf16 workloads round them to
@@ -31,7 +33,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "get", "bf16_bits_from_f32", "f32_from_bf16_bits",
+    "Workload", "WORKLOADS", "get", "bf16_bits_from_f32", "f32_from_bf16_bits", "draw_gate",
     "draw_x", "draw_logits", "draw_expert", "draw_all_experts",
 ]
 
@@ -97,7 +99,7 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- streams
-_X, _LOGITS, _W = 0, 1, 2
+_X, _LOGITS, _W, _GATE = 0, 1, 2, 3
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -120,6 +122,14 @@ def draw_logits(w: Workload) -> np.ndarray:
     if w.zipf:
         z = (z + zipf_bias(w.E)[None, :]).astype(np.float32)
     return bf16_bits_from_f32(z)
+
+
+def draw_gate(w: Workload) -> np.ndarray:
+    """Router gate weights as bf16 bit patterns, [E, H] uint16: N(0, 1/H) in fp32 (standard normal
+    times 1/sqrt(H)), so that with N(0, 1) activations the logits are about N(0, 1), the logit
+    distribution of the drawn-logits workloads."""
+    z = _rng(w.seed, _GATE).standard_normal((w.E, w.H), dtype=np.float32)
+    return bf16_bits_from_f32(z * np.float32(1.0 / math.sqrt(w.H)))
 
 
 def draw_expert(w: Workload, e: int):
