@@ -340,10 +340,16 @@ __device__ __forceinline__ void finalize_chunk_if_last(const GemmParams& p, int 
 }
 
 // ------------------------------------------------------------------------------ small-M
-template <int WF, int MT, bool GATE_UP, int D>
-__global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, int n_blocks) {
+// KS > 1 (few units, 16-row blocks): KS waves share a unit, wave w taking K-steps w, w + KS, ...;
+// their accumulators are added in LDS in wave order (a fixed order) and wave 0 runs the epilogue.
+// With a few hundred single-wave units (a handful of tokens) each wave's K stream is a chain of
+// memory round trips; split over KS waves the chain is KS times shorter.
+template <int WF, int MT, bool GATE_UP, int D, int KS>
+__global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chunks, int n_blocks) {
   static_assert(GATE_UP || MT == 1, "the down epilogue of this launcher handles one 16-row tile");
-  const int lane = threadIdx.x, n = lane & 15, g = lane >> 4;
+  static_assert(KS == 1 || MT == 1, "split K reduces one 16-row tile");
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int wave = KS > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   // Unit order: XCD x = blockIdx % 8 takes the x-th contiguous range of the units that have rows
   // (the grid is sized for the layout's capacity; ranges cut from the real tile count give every
   // XCD the same work, measured 57.9 -> 55.6 us for the 32-token gate_up); units run chunk-major,
@@ -370,8 +376,9 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     // the loads of group k0 + D while multiplying group k0 without any branch, and the last group
     // is peeled. Weight loads of the first group go out before the (dependent) row lookup.
     Stage<WF, MT> buf[D];
+    const int nk = p.NKS / KS;  // K-steps of this wave: global step wave + KS * i
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_b<WF, MT, MT>(p, tr, s, lane, buf[s]);
+    for (int s = 0; s < D; ++s) load_b<WF, MT, MT>(p, tr, wave + KS * s, lane, buf[s]);
     // down: slot id and routing weight of the lane's four output rows, fetched now so the
     // epilogue does not wait for them
     int rsid[4];
@@ -385,17 +392,34 @@ __global__ __launch_bounds__(64) void k_gemm_stream(GemmParams p, int n_chunks, 
     }
     tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_a<WF, MT>(tr, s, buf[s]);
+    for (int s = 0; s < D; ++s) load_a<WF, MT>(tr, wave + KS * s, buf[s]);
     int k0 = 0;
-    for (; k0 + D < p.NKS; k0 += D) {
+    for (; k0 + D < nk; k0 += D) {
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         mma_stage<WF, MT>(buf[s], 8 * g, acc);
-        load_stage<WF, MT>(p, tr, k0 + s + D, lane, buf[s]);
+        load_stage<WF, MT>(p, tr, wave + KS * (k0 + s + D), lane, buf[s]);
       }
     }
 #pragma unroll
     for (int s = 0; s < D; ++s) mma_stage<WF, MT>(buf[s], 8 * g, acc);
+    if constexpr (KS > 1) {
+      __shared__ v4f part[KS][4][64];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) part[wave][f][lane] = acc[0][f];
+      __syncthreads();
+      if (wave != 0) return;  // one 16-row tile per unit (block_m 16): nothing left for the others
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        v4f t = part[0][f][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) {
+          const v4f q = part[w][f][lane];
+          t[0] += q[0]; t[1] += q[1]; t[2] += q[2]; t[3] += q[3];
+        }
+        acc[0][f] = t;
+      }
+    }
     if constexpr (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
     else epilogue_down_rows(p, acc[0], rsid, rw, chunk, n);
   }
@@ -700,6 +724,9 @@ __global__ __launch_bounds__(64) void k_gemm_direct(GemmParams p) {
   }
 }
 
+// Most small-M units (column chunks x capacity tiles) for which the stream launcher splits K.
+constexpr int kSplitKMaxUnits = 1024;
+
 // Deepest register ring (K-steps in flight per wave) that divides the K-step count and keeps two
 // waves per SIMD: fp8 weights fit 3 stages, fp4 4, bf16 2.
 inline int stream_depth(int wf, int nks) {
@@ -713,12 +740,12 @@ inline int stream_depth(int wf, int nks) {
   return 1;
 }
 
-template <int WF, bool GATE_UP, int D>
+template <int WF, bool GATE_UP, int D, int KS = 1>
 hipError_t launch_stream(const GemmParams& p, int n_chunks, int n_blocks, hipStream_t st) {
   const int total = n_chunks * n_blocks;
   const int grid = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D>), dim3(grid), dim3(64), 0, st, p, n_chunks,
-                     n_blocks);
+  hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS>), dim3(grid), dim3(64 * KS), 0, st, p,
+                     n_chunks, n_blocks);
   return hipGetLastError();
 }
 
@@ -740,6 +767,17 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
       hipLaunchKernelGGL((k_gemm_direct<WF, 4, GATE_UP>), dim3(n_chunks, n_blocks), dim3(64), 0, st, p);
     }
     return hipGetLastError();
+  }
+  // Split K over 4 waves when the layout has fewer 16-row tiles than a quarter of the SIMDs' share
+  // (a handful of tokens) and each wave keeps whole ring groups.
+  if (WF != WF_BF16 && p.block_m == 16 && n_chunks * n_blocks <= kSplitKMaxUnits &&
+      p.NKS % 4 == 0) {
+    switch (stream_depth(WF, p.NKS / 4)) {
+      case 4: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 4), 4>(p, n_chunks, n_blocks, st);
+      case 3: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 3), 4>(p, n_chunks, n_blocks, st);
+      case 2: return launch_stream<WF, GATE_UP, 2, 4>(p, n_chunks, n_blocks, st);
+      default: return launch_stream<WF, GATE_UP, 1, 4>(p, n_chunks, n_blocks, st);
+    }
   }
   switch (stream_depth(WF, p.NKS)) {
     case 4: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 4)>(p, n_chunks, n_blocks, st);
