@@ -120,6 +120,38 @@ class GpuWorkload:
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
+    def time_graph(self, steps, warmup):
+        """Average time of one forward per HIP graph replay: one graph per weight copy
+        (captured once, replayed in the same rotation as the eager steps), so the launch overhead
+        of the library's kernels is paid at capture, as a serving loop under graph execution
+        would."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(self.packed)):
+                self.step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(len(self.packed)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graphs
+        return e0.elapsed_time(e1) / steps
+
     def time_stages(self, steps):
         """Average duration of each stage, from events the library records on its stream."""
         torch, B = self.torch, self.B
@@ -161,6 +193,10 @@ def measure(name, steps, warmup):
     res["mfma_frac"] = res["TFLOPs"] / PEAK_MFMA_TFLOPS[w.w_fmt]
     gu_ms = stages["gate_up"]
     decode = w.slots < 16 * (w.E + 1)
+    if decode:   # decode sizes: the same steps replayed from HIP graphs
+        gms = g.time_graph(steps, warmup)
+        res["graph"] = {"ms_per_step": gms, "GBps": by / (gms * 1e-3) / 1e9,
+                        "hbm_frac": by / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if decode:
         ach = gate_up_bytes(w, touched) / (gu_ms * 1e-3) / 1e9
         res["roofline"] = {"kernel": "gate_up", "bound": "hbm", "achieved": ach,
@@ -173,7 +209,8 @@ def measure(name, steps, warmup):
                            "unit": "TFLOP/s", "frac": ach / pk, "flops_per_launch": gate_up_flops(w)}
     log(f"{name}: {ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
         f"{res['TFLOPs']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% MFMA), stages(us) "
-        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items())
+        + (f"; graph replay {res['graph']['ms_per_step'] * 1e3:.1f} us/step" if "graph" in res else ""))
     return g, res
 
 
@@ -273,7 +310,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_mxfp8")
-    ap.add_argument("--extra", default="prefill_mxfp8",
+    ap.add_argument("--extra", default="prefill_mxfp8,wide512_mxfp4_T1,wide512_mxfp4_T6",
                     help="comma-separated extra workloads, 'all', or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -331,7 +368,7 @@ def main():
                    "parallelism": "single GPU (one TP share, all experts resident)"},
         "tflops": head["TFLOPs"], "hbm_frac": head["hbm_frac"], "mfma_frac": head["mfma_frac"],
         "touched_experts": head["touched_experts"], "stage_ms": head["stage_ms"],
-        "roofline": rl, "cpu_baseline": base, "gate": gate,
+        "roofline": rl, "cpu_baseline": base, "graph": head.get("graph"), "gate": gate,
         "workloads": {n: {k: v for k, v in r.items() if k not in ("T", "H", "E", "top_k",
                                                                   "shared_experts")}
                       for n, r in others.items()},

@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
+#include <utility>
 
 #include "device.h"
 #include "kernels.h"
@@ -53,6 +54,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uin
                                            0x00020000);
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop whose index is a
+// compile-time constant in the body (register slots picked by it stay registers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 // Per-wave view of its tile: descriptors of the expert's weights / scales and of the activation
 // rows, the lane's byte offset into its A row (per 16-row tile mt) and the wave's first fragment.
@@ -574,7 +586,7 @@ struct TileLds {
   static constexpr int bytes = as + kTileWaves * 256;
 };
 
-template <int WF, bool GATE_UP>
+template <int WF, bool GATE_UP, bool PIPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   using L = TileLds;
@@ -660,7 +672,39 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   // activation loads are invisible to it). The
   // loop runs over pairs of steps so that the register slots are compile-time; after an odd step
   // count the last step runs alone (its loads were issued by the step before it).
+  // PIPE: the next step's weights go out first, so they have a whole step to arrive, and the
+  // activation fragments are read one 16-row group ahead of their MFMAs (two register sets).
+  auto a_frag = [&](int stage, int mt, v8i& a8, uint32_t& sa) {
+    const uint8_t* st = lds + stage * L::bytes;
+    const uint8_t* base = st + L::a + n * kLdsPitch;
+    a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
+    a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
+    sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
+  };
+  auto step_pipe = [&](auto SLOT, int ks) {
+    constexpr int s = decltype(SLOT)::value;
+    const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
+    TileRows<1> tn = tr;
+    if (oob) tn.w = raw_rsrc(p.w, 0);
+    load_b<WF, 1, 1>(p, tn, ks + 1 < nks ? ks + 1 : 0, lane, bs[1 - s]);
+    __builtin_amdgcn_sched_barrier(0);
+    v8i a8[2];
+    uint32_t sa[2];
+    a_frag(s, 0, a8[0], sa[0]);
+    static_for<MT>([&](auto MTI) {
+      constexpr int mt = decltype(MTI)::value;
+      if constexpr (mt + 1 < MT) a_frag(s, mt + 1, a8[(mt + 1) & 1], sa[(mt + 1) & 1]);
+      if constexpr (mt == 1) issue_a(1 - s, ks + 1, oob);
+      mma_frags<WF>(a8[mt & 1], (int)(sa[mt & 1] >> (8 * g)), bs[s].b, (int)bs[s].sb, acc[mt]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_loads_barrier<0>();
+  };
   auto step = [&](auto SLOT, int ks) {
+    if constexpr (PIPE) {
+      step_pipe(SLOT, ks);
+      return;
+    }
     constexpr int s = decltype(SLOT)::value;
     const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
     compute(s, bs[s], 0, 2);
@@ -727,10 +771,12 @@ __global__ __launch_bounds__(64) void k_gemm_direct(GemmParams p) {
 // Most small-M units (column chunks x capacity tiles) for which the stream launcher splits K.
 constexpr int kSplitKMaxUnits = 1024;
 
-// Deepest register ring (K-steps in flight per wave) that divides the K-step count and keeps two
-// waves per SIMD: fp8 weights fit 3 stages, fp4 4, bf16 2.
+// Deepest register ring (K-steps in flight per wave) that divides the K-step count: fp8 weights
+// 3 stages, fp4 2, bf16 2. For fp4 the shallower ring raises occupancy from three to four waves
+// per SIMD; measured on 128 tokens, hidden 3072, intermediate 768: block 125 -> 119 us (4 stages
+// against 2; 1 stage 121 us); for fp8 1 to 3 stages give the same time.
 inline int stream_depth(int wf, int nks) {
-  int dmax = wf == WF_BF16 ? 2 : (wf == WF_FP8 ? 3 : 4);
+  int dmax = wf == WF_BF16 ? 2 : (wf == WF_FP8 ? 3 : 2);
   if (const char* env = getenv("MXMOE_STREAM_DEPTH")) {  // A/B knob: 1..4
     int d = atoi(env);
     if (d >= 1 && d <= 4) dmax = wf == WF_BF16 ? (d < 2 ? d : 2) : d;
@@ -738,6 +784,14 @@ inline int stream_depth(int wf, int nks) {
   for (int d = dmax; d > 1; --d)
     if (nks % d == 0) return d;
   return 1;
+}
+
+// Pipelined K-steps in the large-M launcher: measured on the 8K-token prefill, gate_up 233 -> 223
+// us (fp8) and on 4096 tokens x 512 experts 195 -> 184 us (fp4); down 101 -> 99 us (fp4) but
+// 203 -> 205 us (fp8, three K-steps), where it stays off.
+inline bool tile_pipe(bool gate_up, int wf) {
+  if (const char* env = getenv("MXMOE_TILE_PIPE")) return atoi(env) != 0;  // A/B knob
+  return gate_up || wf == WF_FP4;
 }
 
 template <int WF, bool GATE_UP, int D, int KS = 1>
@@ -761,8 +815,12 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
       const int sub_shift = p.block_m == kTileM ? 0 : 1;
       const int total = n_tile_chunks * (n_blocks << sub_shift);
       const dim3 grid(((total + 7) / 8) * 8), block(256);
-      hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP>), grid, block, 0, st, p, n_tile_chunks,
-                         n_blocks << sub_shift, sub_shift);
+      if (tile_pipe(GATE_UP, WF))
+        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, true>), grid, block, 0, st, p, n_tile_chunks,
+                           n_blocks << sub_shift, sub_shift);
+      else
+        hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, false>), grid, block, 0, st, p, n_tile_chunks,
+                           n_blocks << sub_shift, sub_shift);
     } else {
       hipLaunchKernelGGL((k_gemm_direct<WF, 4, GATE_UP>), dim3(n_chunks, n_blocks), dim3(64), 0, st, p);
     }

@@ -357,6 +357,43 @@ def test_forward_slots_deterministic_and_permutation_invariant():
     assert torch.equal(yp.view(torch.int16), y1[torch.from_numpy(perm).to(DEV)].view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny_bf16", "decode_mxfp8", "wide512_mxfp4_T1",
+                                  "wide512_mxfp4_T6"])
+def test_forward_graph_replay(name):
+    # One forward captured in a HIP graph (the library only enqueues kernels on the caller's
+    # stream) and replayed on new inputs written into the captured buffers, with eager forwards
+    # and host synchronisations between the replays: every replay equals the eager result bit for
+    # bit (same kernels, fixed-order combine).
+    _say("graph replay", name)
+    w, xb, lb = inputs(name)
+    _, packed = packed_weights(name)
+    shape = shape_of(w)
+    rng = np.random.default_rng(7)
+    draws = [(xb, lb)] + [(xb[rng.permutation(w.T)], lb[rng.permutation(w.T)]) for _ in range(2)]
+    xs, ls = bf16_tensor(xb), bf16_tensor(lb)
+    ys = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+    wss = torch.empty(B.mxmoe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.mxmoe_forward(shape, xs, ls, packed, y=ys, workspace=wss)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.mxmoe_forward(shape, xs, ls, packed, y=ys, workspace=wss)
+    torch.cuda.synchronize()
+    for xr, lr in draws:
+        ref = B.mxmoe_forward(shape, bf16_tensor(xr), bf16_tensor(lr), packed)
+        torch.cuda.synchronize()
+        xs.copy_(bf16_tensor(xr))
+        ls.copy_(bf16_tensor(lr))
+        ys.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys.view(torch.int16), ref.view(torch.int16))
+
+
 # ------------------------------------------------------------------------------- edge shapes
 @pytest.mark.parametrize("T,H,E,k,I,fmt", [
     (1, 128, 1, 1, 32, "mxfp8"),      # one token, one routed expert
