@@ -152,6 +152,33 @@ class GpuWorkload:
         del graphs
         return e0.elapsed_time(e1) / steps
 
+    def time_each(self, steps):
+        """Per-step durations from one event pair around each call (the pair's own cost included):
+        the spread of the step time."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            self.step(i)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    def time_warm(self, steps):
+        """Every call on the same weight copy (for context: whatever of it the caches keep)."""
+        torch = self.torch
+        for _ in range(3):
+            self.step(0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            self.step(0)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def time_stages(self, steps):
         """Average duration of each stage, from events the library records on its stream."""
         torch, B = self.torch, self.B
@@ -176,6 +203,8 @@ class GpuWorkload:
 def measure(name, steps, warmup):
     g = GpuWorkload(name)
     ms, wall_ms = g.time_steps(steps, warmup)
+    each = g.time_each(max(10, min(steps, 50)))
+    warm_ms = g.time_warm(max(10, min(steps, 50)))
     stages = g.time_stages(max(10, min(steps, 50)))
     touched = g.touched_experts()
     w = g.w
@@ -185,6 +214,8 @@ def measure(name, steps, warmup):
         "T": w.T, "H": w.H, "E": w.E, "top_k": w.top_k, "shared_experts": 1, "I": w.I,
         "w_fmt": w.w_fmt, "act_fmt": w.act_fmt, "zipf": w.zipf, "touched_experts": touched,
         "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+        "step_ms_p10_p50_p90": [float(np.percentile(each, q)) for q in (10, 50, 90)],
+        "warm_ms_per_step": warm_ms,
         "algorithmic_MB": by / 1e6, "GFLOP": fl / 1e9,
         "GBps": by / (ms * 1e-3) / 1e9, "TFLOPs": fl / (ms * 1e-3) / 1e12,
         "stage_ms": stages,
@@ -210,7 +241,9 @@ def measure(name, steps, warmup):
     log(f"{name}: {ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
         f"{res['TFLOPs']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% MFMA), stages(us) "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items())
-        + (f"; graph replay {res['graph']['ms_per_step'] * 1e3:.1f} us/step" if "graph" in res else ""))
+        + (f"; graph replay {res['graph']['ms_per_step'] * 1e3:.1f} us/step" if "graph" in res else "")
+        + "; per-step p10/p50/p90 " + "/".join(f"{v * 1e3:.1f}" for v in res["step_ms_p10_p50_p90"])
+        + f" us; warm {warm_ms * 1e3:.1f} us")
     return g, res
 
 
@@ -367,6 +400,7 @@ def main():
                    ("T", "H", "E", "top_k", "shared_experts", "I", "w_fmt", "act_fmt", "zipf")},
                    "parallelism": "single GPU (one TP share, all experts resident)"},
         "tflops": head["TFLOPs"], "hbm_frac": head["hbm_frac"], "mfma_frac": head["mfma_frac"],
+        "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"], "warm_ms_per_step": head["warm_ms_per_step"],
         "touched_experts": head["touched_experts"], "stage_ms": head["stage_ms"],
         "roofline": rl, "cpu_baseline": base, "graph": head.get("graph"), "gate": gate,
         "workloads": {n: {k: v for k, v in r.items() if k not in ("T", "H", "E", "top_k",

@@ -352,6 +352,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.out32 = out32;
   g.combine = P.combine;
   g.T = P.T;
+  g.xcd_order = 1;
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
@@ -365,6 +366,12 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
+    // Large-M gate_up with fewer than two 128-row tiles per expert on average (many experts, each
+    // a tile of mostly padding): plain linear unit order. Measured at 4096 tokens over 512 experts
+    // (Zipf popularity; median touched expert 7.5 rows): gate_up 182 -> 112-119 us; at 8192 tokens
+    // over 128 experts (~570 rows each) the per-XCD ranges stay better (222 against 238 us).
+    gu.xcd_order = P.large && P.S < 256 * P.E1 ? 0 : 1;
+    if (const char* env = getenv("MXMOE_XCD_ORDER")) gu.xcd_order = atoi(env);  // A/B knob
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);

@@ -369,8 +369,8 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
   const int nb = *p.num_post_pad / p.block_m;
   const int total = n_chunks * nb;
   const int per_xcd = (total + 7) >> 3;
-  if ((int)(blockIdx.x >> 3) >= per_xcd) return;
-  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (p.xcd_order && (int)(blockIdx.x >> 3) >= per_xcd) return;
+  const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
   if (u >= total) return;
   const int chunk = u / nb, blk = u - chunk * nb;
   const int r0 = blk * p.block_m;
@@ -596,7 +596,7 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = n_chunks * n_blocks;
   const int per_xcd = (total + 7) >> 3;
-  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
   if (u >= total) return;
   // Unit order inside an XCD's range: gate_up runs tile-major (the column chunks of a tile are
   // adjacent, so the gathered activation tile is fetched once and reused from L2); down runs

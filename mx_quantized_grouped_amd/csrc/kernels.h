@@ -113,6 +113,9 @@ struct GemmParams {
   uint16_t* y;
   int32_t* chunk_done;
   int T;
+  // 1: units in contiguous per-XCD ranges (the tiles of one expert on one XCD's L2); 0: plain
+  // linear order over the grid (consecutive workgroups round-robin over the XCDs)
+  int xcd_order;
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
