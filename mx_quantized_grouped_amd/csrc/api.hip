@@ -353,6 +353,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.combine = P.combine;
   g.T = P.T;
   g.xcd_order = 1;
+  g.xcd_run = 1;
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
@@ -366,12 +367,18 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
-    // Large-M gate_up with fewer than two 128-row tiles per expert on average (many experts, each
-    // a tile of mostly padding): plain linear unit order. Measured at 4096 tokens over 512 experts
-    // (Zipf popularity; median touched expert 7.5 rows): gate_up 182 -> 112-119 us; at 8192 tokens
-    // over 128 experts (~570 rows each) the per-XCD ranges stay better (222 against 238 us).
-    gu.xcd_order = P.large && P.S < 256 * P.E1 ? 0 : 1;
-    if (const char* env = getenv("MXMOE_XCD_ORDER")) gu.xcd_order = atoi(env);  // A/B knob
+    // Large-M gate_up: each XCD takes runs of 4 tiles (all column chunks of each) in turn, so every
+    // XCD works through the whole expert list (popular and one-tile experts alike) while a run
+    // still shares its activation tiles and expert weights in one L2. Measured, gate_up: 8192
+    // tokens x 128 experts 226 us with contiguous per-XCD ranges, 239 in plain linear order, 208
+    // with runs of 4 tiles; 4096 tokens x 512 experts (median touched expert 7.5 rows) 182, 117
+    // and 115 us. The down pass keeps the per-XCD ranges (runs of 1-32 units: no better).
+    if (P.large) {
+      gu.xcd_order = 0;
+      gu.xcd_run = P.I >= 128 ? 4 * (P.I / 128) : 1;
+    }
+    if (const char* env = getenv("MXMOE_XCD_ORDER_GU")) gu.xcd_order = atoi(env);  // A/B knobs
+    if (const char* env = getenv("MXMOE_XCD_RUN_GU")) gu.xcd_run = atoi(env) > 0 ? atoi(env) : 1;
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);

@@ -596,7 +596,9 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = n_chunks * n_blocks;
   const int per_xcd = (total + 7) >> 3;
-  const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
+  // workgroups go round-robin over the 8 XCDs: XCD x = blockIdx % 8 runs positions blockIdx / 8
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3, run = p.xcd_run;
+  const int u = p.xcd_order ? xcd * per_xcd + pos : (pos / run) * (8 * run) + xcd * run + pos % run;
   if (u >= total) return;
   // Unit order inside an XCD's range: gate_up runs tile-major (the column chunks of a tile are
   // adjacent, so the gathered activation tile is fetched once and reused from L2); down runs
@@ -814,7 +816,8 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
     if (tiles) {
       const int sub_shift = p.block_m == kTileM ? 0 : 1;
       const int total = n_tile_chunks * (n_blocks << sub_shift);
-      const dim3 grid(((total + 7) / 8) * 8), block(256);
+      const int gq = p.xcd_order ? 8 : 8 * p.xcd_run;  // whole rounds of the unit mapping
+      const dim3 grid(((total + gq - 1) / gq) * gq), block(256);
       if (tile_pipe(GATE_UP, WF))
         hipLaunchKernelGGL((k_gemm_tile<W, GATE_UP, true>), grid, block, 0, st, p, n_tile_chunks,
                            n_blocks << sub_shift, sub_shift);

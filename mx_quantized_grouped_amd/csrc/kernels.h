@@ -116,6 +116,9 @@ struct GemmParams {
   // 1: units in contiguous per-XCD ranges (the tiles of one expert on one XCD's L2); 0: plain
   // linear order over the grid (consecutive workgroups round-robin over the XCDs)
   int xcd_order;
+  // large-M launcher, xcd_order 0: each XCD takes runs of xcd_run consecutive units in turn
+  // (1: plain linear order); the grid is a whole number of 8 * xcd_run workgroups
+  int xcd_run;
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
