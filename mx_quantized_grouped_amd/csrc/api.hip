@@ -353,7 +353,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.combine = P.combine;
   g.T = P.T;
   g.xcd_order = 1;
-  g.xcd_run = 1;
+  if (const char* env = getenv("MXMOE_XCD_ORDER")) g.xcd_order = atoi(env) != 0;  // A/B knob
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
@@ -367,18 +367,9 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
-    // Large-M gate_up: each XCD takes runs of 4 tiles (all column chunks of each) in turn, so every
-    // XCD works through the whole expert list (popular and one-tile experts alike) while a run
-    // still shares its activation tiles and expert weights in one L2. Measured, gate_up: 8192
-    // tokens x 128 experts 226 us with contiguous per-XCD ranges, 239 in plain linear order, 208
-    // with runs of 4 tiles; 4096 tokens x 512 experts (median touched expert 7.5 rows) 182, 117
-    // and 115 us. The down pass keeps the per-XCD ranges (runs of 1-32 units: no better).
-    if (P.large) {
-      gu.xcd_order = 0;
-      gu.xcd_run = P.I >= 128 ? 4 * (P.I / 128) : 1;
-    }
-    if (const char* env = getenv("MXMOE_XCD_ORDER_GU")) gu.xcd_order = atoi(env);  // A/B knobs
-    if (const char* env = getenv("MXMOE_XCD_RUN_GU")) gu.xcd_run = atoi(env) > 0 ? atoi(env) : 1;
+    // large-M unit order: runs of 4 tiles (all their 256-column chunks) per XCD turn
+    gu.xcd_run = P.I >= 128 ? 4 * (P.I / 128) : 1;
+    if (const char* env = getenv("MXMOE_XCD_RUN_GU")) gu.xcd_run = atoi(env);  // A/B knob
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);
@@ -392,6 +383,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.as_bytes = (uint32_t)((size_t)P.cap * P.srs_I);
     dn.w = (const uint8_t*)w2_p;
     dn.ws = (const uint8_t*)s2_p;
+    dn.xcd_run = P.H >= 256 ? 4 * (P.H / 256) : 1;
+    if (const char* env = getenv("MXMOE_XCD_RUN_DN")) dn.xcd_run = atoi(env);  // A/B knob
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
     if (P.fuse_final) {

@@ -113,11 +113,10 @@ struct GemmParams {
   uint16_t* y;
   int32_t* chunk_done;
   int T;
-  // 1: units in contiguous per-XCD ranges (the tiles of one expert on one XCD's L2); 0: plain
-  // linear order over the grid (consecutive workgroups round-robin over the XCDs)
+  // small-M launcher: 1 units in contiguous per-XCD ranges, 0 plain linear order over the grid
   int xcd_order;
-  // large-M launcher, xcd_order 0: each XCD takes runs of xcd_run consecutive units in turn
-  // (1: plain linear order); the grid is a whole number of 8 * xcd_run workgroups
+  // large-M launcher: each XCD takes runs of xcd_run consecutive units in turn (1: plain linear
+  // order over the grid; 0: one contiguous range per XCD)
   int xcd_run;
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
