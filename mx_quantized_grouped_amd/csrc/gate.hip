@@ -3,14 +3,18 @@
 // trễ giải mã lên 54% trên 4 GPU Blackwell" ("Sửa thước đo trước khi sửa máy"), whose 2.6 MB
 // gate-weight kernel took 7 us with its weights in L2 and 11 us with them cold there.
 //
-// A workgroup of 4 waves computes a 16-token x (16 F)-expert tile. The waves split the K-steps of
-// 32 (wave w takes steps w, w + 4, ...), and their partial sums are added in LDS in wave order, so
-// the result does not depend on timing. Each wave keeps kGateDepth K-steps of loads in flight. The
-// expert-tile width grows with the batch: F = 1 up to 64 tokens (the weight stream spread over the
-// most CUs: 8 us for 32 tokens, hidden 3072, 128 experts), F = 2 up to 2048 (10 us for 1024
-// tokens), F = 4 beyond (56 us for 8192). Each load instruction reads 64 bytes of each of 16 rows
-// (the MFMA operand layout), so at large batches the number of cache lines in flight, not
-// bandwidth, limits the kernel; staging row-contiguous tiles through LDS would lift that.
+// A workgroup of 4 waves computes a (16 TM)-token x (16 F)-expert tile. The waves split the K-steps
+// of 32 (wave w takes steps w, w + 4, ...), and their partial sums are added in LDS in wave order,
+// so the result does not depend on timing. Each wave keeps 4 (or, for tiles of more than 4
+// fragments, 2) K-steps of loads in flight. Each load instruction reads 64 bytes of each of 16
+// rows (the MFMA operand layout). The tile grows with the batch (measured, hidden 3072 and 128
+// experts unless stated): one fragment up to 256 tokens (the weight stream spread over the most
+// CUs: 7.1 us for 32 tokens, 7.4 us for 128, against 9.7 us with 16 x 32 tiles); 16 x 32 up to
+// 2048 tokens; beyond, 64 x 64 tiles (8192 tokens: 26.5 us, against 56 us for 16 x 64 tiles, which
+// re-read the weights for every 16 tokens) and, from 512 experts on, 64 x 128 (4096 tokens, hidden
+// 2048: 28.8 us against 33.4 us for 64 x 64 and 73 us for 16 x 64).
+#include <cstdlib>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -29,78 +33,93 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gate_rsrc(const void* base, ui
 
 // OUT_F32: fp32 logits, else bf16 (round to nearest even). Rows past T and experts past E read as
 // zero (buffer range checks) and are not stored.
-template <int F, bool OUT_F32>
+// TM 16-token fragments x F 16-expert fragments per workgroup.
+template <int TM, int F, bool OUT_F32>
 __global__ __launch_bounds__(256) void k_gate(const uint16_t* x, const uint16_t* wg, int T, int H,
                                               int E, void* out) {
-  __shared__ v4f part[kGateWaves][F][64];
+  __shared__ v4f part[kGateWaves][TM * F][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kGateRows, e0 = blockIdx.y * (16 * F);
+  const int t0 = blockIdx.x * (kGateRows * TM), e0 = blockIdx.y * (16 * F);
   const uint32_t row_bytes = (uint32_t)H * 2u;
-  const int tr = min(kGateRows, T - t0), er = min(16 * F, E - e0);
+  const int tr = min(kGateRows * TM, T - t0), er = min(16 * F, E - e0);
   const auto ra = gate_rsrc(x + (size_t)t0 * H, (uint32_t)tr * row_bytes);
   const auto rb = gate_rsrc(wg + (size_t)e0 * H, (uint32_t)er * row_bytes);
   // lane (n, g) holds K elements 8 g .. 8 g + 7 of a step: row n of the token fragment, row n of
   // each expert fragment
   const uint32_t aoff = (uint32_t)n * row_bytes + 16u * g;
   const int nsteps = H / 32;
-  v4f acc[F];
+  v4f acc[TM][F];
 #pragma unroll
-  for (int f = 0; f < F; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = wave; k0 < nsteps; k0 += kGateWaves * kGateDepth) {
-    v4i a[kGateDepth], b[kGateDepth][F];
+  for (int m = 0; m < TM; ++m)
 #pragma unroll
-    for (int d = 0; d < kGateDepth; ++d) {  // every load of the batch before the first MFMA
+    for (int f = 0; f < F; ++f) acc[m][f] = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int D = TM * F > 4 ? 2 : kGateDepth;  // K-steps of loads in flight per wave
+  for (int k0 = wave; k0 < nsteps; k0 += kGateWaves * D) {
+    v4i a[D][TM], b[D][F];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {  // every load of the batch before the first MFMA
       // steps past the end load out of range: zeros, so the MFMAs below need no branch (a branch
       // let the compiler sink each load next to its use)
       const int k = k0 + kGateWaves * d;
       const uint32_t oob = k < nsteps ? 0u : 0x80000000u;
       const int soff = (k < nsteps ? k : 0) * 64;
-      a[d] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff | oob, soff, 0);
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+        a[d][m] = __builtin_amdgcn_raw_buffer_load_b128(ra, (aoff + 16u * m * row_bytes) | oob,
+                                                        soff, 0);
 #pragma unroll
       for (int f = 0; f < F; ++f)
         b[d][f] = __builtin_amdgcn_raw_buffer_load_b128(rb, (aoff + 16u * f * row_bytes) | oob,
                                                         soff, 0);
     }
 #pragma unroll
-    for (int d = 0; d < kGateDepth; ++d) {
+    for (int d = 0; d < D; ++d) {
 #pragma unroll
-      for (int f = 0; f < F; ++f)
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[d]),
-                                                         __builtin_bit_cast(v8bf, b[d][f]),
-                                                         acc[f], 0, 0, 0);
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+          acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[d][m]),
+                                                              __builtin_bit_cast(v8bf, b[d][f]),
+                                                              acc[m][f], 0, 0, 0);
     }
   }
-  // C[4 g + i][n] of fragment f, stored by wave f after adding the waves' partial sums in order
-  auto store = [&](int f, const v4f& v) {
+  // C[4 g + i][n] of token fragment m, expert fragment f; fragment j = m * F + f is stored by wave
+  // j % 4 after adding the waves' partial sums in wave order
+  auto store = [&](int j, const v4f& v) {
+    const int m = j / F, f = j - m * F;
     const int e = e0 + 16 * f + n;
     if (e >= E) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * g + i;
+      const int t = t0 + 16 * m + 4 * g + i;
       if (t >= T) continue;
       if (OUT_F32) ((float*)out)[(size_t)t * E + e] = v[i];
       else ((uint16_t*)out)[(size_t)t * E + e] = (uint16_t)f32_to_bf16_bits(v[i]);
     }
   };
 #pragma unroll
-  for (int f = 0; f < F; ++f) part[wave][f][lane] = acc[f];
-  __syncthreads();
-  if (wave >= F) return;
-  v4f s = part[0][wave][lane];
+  for (int m = 0; m < TM; ++m)
 #pragma unroll
-  for (int w = 1; w < kGateWaves; ++w) {
-    const v4f q = part[w][wave][lane];
-    s[0] += q[0]; s[1] += q[1]; s[2] += q[2]; s[3] += q[3];
+    for (int f = 0; f < F; ++f) part[wave][m * F + f][lane] = acc[m][f];
+  __syncthreads();
+  for (int j = wave; j < TM * F; j += kGateWaves) {
+    v4f s = part[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kGateWaves; ++w) {
+      const v4f q = part[w][j][lane];
+      s[0] += q[0]; s[1] += q[1]; s[2] += q[2]; s[3] += q[3];
+    }
+    store(j, s);
   }
-  store(wave, s);
 }
 
-template <int F>
+template <int TM, int F>
 hipError_t launch_gate_f(const uint16_t* x, const uint16_t* wg, int T, int H, int E, bool f32,
                          void* out, hipStream_t st) {
-  const dim3 grid((T + kGateRows - 1) / kGateRows, (E + 16 * F - 1) / (16 * F)), block(256);
-  if (f32) hipLaunchKernelGGL((k_gate<F, true>), grid, block, 0, st, x, wg, T, H, E, out);
-  else hipLaunchKernelGGL((k_gate<F, false>), grid, block, 0, st, x, wg, T, H, E, out);
+  const dim3 grid((T + kGateRows * TM - 1) / (kGateRows * TM), (E + 16 * F - 1) / (16 * F));
+  const dim3 block(256);
+  if (f32) hipLaunchKernelGGL((k_gate<TM, F, true>), grid, block, 0, st, x, wg, T, H, E, out);
+  else hipLaunchKernelGGL((k_gate<TM, F, false>), grid, block, 0, st, x, wg, T, H, E, out);
   return hipGetLastError();
 }
 
@@ -108,9 +127,23 @@ hipError_t launch_gate_f(const uint16_t* x, const uint16_t* wg, int T, int H, in
 
 hipError_t launch_gate(const uint16_t* x, const uint16_t* wg, int T, int H, int E, bool f32,
                        void* out, hipStream_t st) {
-  if (T <= 64) return launch_gate_f<1>(x, wg, T, H, E, f32, out, st);
-  if (T <= 2048) return launch_gate_f<2>(x, wg, T, H, E, f32, out, st);
-  return launch_gate_f<4>(x, wg, T, H, E, f32, out, st);
+  int cfg = T <= 256 ? 11 : (T <= 2048 ? 12 : (E >= 512 ? 48 : 44));
+  if (const char* env = getenv("MXMOE_GATE_TILE")) cfg = atoi(env);  // A/B knob: 10 * TM + F
+  switch (cfg) {
+    case 11: return launch_gate_f<1, 1>(x, wg, T, H, E, f32, out, st);
+    case 12: return launch_gate_f<1, 2>(x, wg, T, H, E, f32, out, st);
+    case 14: return launch_gate_f<1, 4>(x, wg, T, H, E, f32, out, st);
+    case 22: return launch_gate_f<2, 2>(x, wg, T, H, E, f32, out, st);
+    case 24: return launch_gate_f<2, 4>(x, wg, T, H, E, f32, out, st);
+    case 28: return launch_gate_f<2, 8>(x, wg, T, H, E, f32, out, st);
+    case 42: return launch_gate_f<4, 2>(x, wg, T, H, E, f32, out, st);
+    case 44: return launch_gate_f<4, 4>(x, wg, T, H, E, f32, out, st);
+    case 48: return launch_gate_f<4, 8>(x, wg, T, H, E, f32, out, st);
+    case 84: return launch_gate_f<8, 4>(x, wg, T, H, E, f32, out, st);
+    case 21: return launch_gate_f<2, 1>(x, wg, T, H, E, f32, out, st);
+    case 41: return launch_gate_f<4, 1>(x, wg, T, H, E, f32, out, st);
+    default: return launch_gate_f<1, 4>(x, wg, T, H, E, f32, out, st);
+  }
 }
 
 }  // namespace mxmoe

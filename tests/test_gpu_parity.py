@@ -107,7 +107,9 @@ def _gate_bound(xb, gb):
 
 
 @pytest.mark.parametrize("T,H,E", [(32, 3072, 128), (8192, 3072, 128), (6, 2048, 512),
-                                   (1, 2048, 512), (37, 96, 70), (100, 64, 1), (65, 128, 130)])
+                                   (1, 2048, 512), (37, 96, 70), (100, 64, 1), (65, 128, 130),
+                                   (4096, 2048, 512), (300, 256, 130), (2100, 96, 520),
+                                   (3000, 64, 200)])
 def test_gate_parity(T, H, E):
     _say("gate", T, H, E)
     wl = workloads.Workload(f"gate_{T}_{H}_{E}", T, H, E, 1, 128, "mxfp8", "mxfp8", False, 9)
