@@ -353,6 +353,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.combine = P.combine;
   g.T = P.T;
   g.xcd_order = 1;
+  g.w_nt = 1;
+  if (const char* env = getenv("MXMOE_W_NT")) g.w_nt = atoi(env) != 0;  // A/B knob
   if (const char* env = getenv("MXMOE_XCD_ORDER")) g.xcd_order = atoi(env) != 0;  // A/B knob
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {

@@ -1,6 +1,8 @@
 // Final rounding of the combined output to bf16. With per-slot rows (fp32 or bf16) the k+1 slot
 // contributions of a token are summed here in fp32 in slot order (a fixed order, so the result is
 // reproducible); with the atomic combine the token-major fp32 accumulator is only converted.
+#include <cstdlib>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -13,7 +15,7 @@ namespace {
 constexpr int kBatch = 9;
 
 // One thread per 8 consecutive output columns.
-template <int COMBINE>
+template <int COMBINE, bool NT>
 __global__ __launch_bounds__(256) void k_finalize(const void* out, int T, int H, int k1,
                                                   uint16_t* y) {
   const int per_row = H / 8;
@@ -48,8 +50,10 @@ __global__ __launch_bounds__(256) void k_finalize(const void* out, int T, int H,
     for (int j0 = 0; j0 < k1; j0 += kBatch) {  // a batch of slot rows in flight, then the adds
       v4i q[kBatch];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b)  // indices past the last slot re-read it (added as zero)
-        q[b] = *(const v4i*)(out16 + (t * k1 + min(j0 + b, k1 - 1)) * H + c);
+      for (int b = 0; b < kBatch; ++b) {  // indices past the last slot re-read it (added as zero)
+        const v4i* src = (const v4i*)(out16 + (t * k1 + min(j0 + b, k1 - 1)) * H + c);
+        q[b] = NT ? __builtin_nontemporal_load(src) : *src;
+      }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const bool on = j0 + b < k1;
@@ -81,9 +85,14 @@ hipError_t launch_finalize(const void* out, int T, int H, int k1, int combine, u
   size_t n = (size_t)T * (H / 8);
   if (n == 0) return hipSuccess;
   dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  if (combine == 1) hipLaunchKernelGGL(k_finalize<1>, grid, block, 0, st, out, T, H, k1, y);
-  else if (combine == 3) hipLaunchKernelGGL(k_finalize<3>, grid, block, 0, st, out, T, H, k1, y);
-  else hipLaunchKernelGGL(k_finalize<2>, grid, block, 0, st, out, T, H, k1, y);
+  // bf16 slot rows are read once: non-temporal loads keep them from displacing cached data.
+  // Measured at 8K tokens (hidden 3072, 9 slots): 105 -> 84 us (non-temporal y stores as well: 89).
+  const char* env = getenv("MXMOE_NT");  // A/B knob: 0 plain loads
+  const bool nt = env ? atoi(env) != 0 : true;
+  if (combine == 1) hipLaunchKernelGGL((k_finalize<1, false>), grid, block, 0, st, out, T, H, k1, y);
+  else if (combine == 3 && nt) hipLaunchKernelGGL((k_finalize<3, true>), grid, block, 0, st, out, T, H, k1, y);
+  else if (combine == 3) hipLaunchKernelGGL((k_finalize<3, false>), grid, block, 0, st, out, T, H, k1, y);
+  else hipLaunchKernelGGL((k_finalize<2, false>), grid, block, 0, st, out, T, H, k1, y);
   return hipGetLastError();
 }
 

@@ -118,6 +118,7 @@ struct GemmParams {
   // large-M launcher: each XCD takes runs of xcd_run consecutive units in turn (1: plain linear
   // order over the grid; 0: one contiguous range per XCD)
   int xcd_run;
+  int w_nt;  // small-M launcher: weight loads with the non-temporal hint
 };
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
