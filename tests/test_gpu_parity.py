@@ -396,6 +396,30 @@ def test_forward_graph_replay(name):
         assert torch.equal(ys.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["prefill_mxfp8", "wide512_mxfp4_T4096"])
+def test_forward_unit_order_invariant(name):
+    # The large-M launcher's unit order (runs of units per XCD turn; 0 = one contiguous range per
+    # XCD, 1 = linear, 5 = runs that do not divide the unit count) only changes which workgroup
+    # computes which output tile: every order must give the library's output bit for bit, so the
+    # mapping covers every unit exactly once.
+    import os
+    _say("unit order", name)
+    w, xb, lb = inputs(name)
+    _, packed = packed_weights(name)
+    shape = shape_of(w)
+    x, lg = bf16_tensor(xb), bf16_tensor(lb)
+    ref = B.mxmoe_forward(shape, x, lg, packed)
+    for run in ("0", "1", "5"):
+        os.environ["MXMOE_XCD_RUN_GU"] = run
+        os.environ["MXMOE_XCD_RUN_DN"] = run
+        try:
+            y = B.mxmoe_forward(shape, x, lg, packed)
+        finally:
+            del os.environ["MXMOE_XCD_RUN_GU"], os.environ["MXMOE_XCD_RUN_DN"]
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), run
+
+
 # ------------------------------------------------------------------------------- edge shapes
 @pytest.mark.parametrize("T,H,E,k,I,fmt", [
     (1, 128, 1, 1, 32, "mxfp8"),      # one token, one routed expert
