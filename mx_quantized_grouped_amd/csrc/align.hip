@@ -56,10 +56,11 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
 // Pass 2 (one workgroup): totals, padded offsets and layout outputs; start[c * E1 + e] becomes the
 // absolute start of the (chunk c, expert e) piece. Threads split into (expert, segment of chunks)
 // pairs so the chunk histograms are walked in parallel. When the histograms fit (up to 28 Ki
-// counts), they are first copied into LDS with coalesced loads issued in batches of 8 per thread
-// (a plain copy loop waits for each load before issuing the next: one memory latency per
-// iteration); walked in global memory, the per-thread chain of loads made this pass take 16 us
-// for an 8K-token batch.
+// counts), they are first copied into LDS with coalesced loads all issued before the first LDS
+// store (a plain copy loop waits for each load before issuing the next: one memory latency per
+// iteration; batches of 8 per thread still took three memory latencies for 4096 tokens over 512
+// experts); walked in global memory, the per-thread chain of loads made this pass take 16 us for
+// an 8K-token batch.
 constexpr int kScanLdsCounts = 28 * 1024;
 __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
                                                               int32_t* __restrict__ start,
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
   const int nh = nchunks * E1;
   const int32_t* hist = hist_g;
   if (nh <= kScanLdsCounts) {
-    constexpr int kB = 8;
+    constexpr int kB = kScanLdsCounts / kAlignThreads;  // every load in one batch
     for (int base = t; base < nh; base += kB * kAlignThreads) {
       int v[kB];
 #pragma unroll
