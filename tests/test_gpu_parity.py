@@ -473,6 +473,31 @@ def test_forward_wide_tiles(T, H, E, k, I, fmt):
         assert tolerance_ok(st), (opt.combine, st)
 
 
+# Degenerate routing: equal logits send every token to experts 0 .. k-1 (ties go to the lower
+# index), so two experts and the shared one hold every slot and the rest are untouched: the
+# largest per-expert row counts the layout can have, on both launchers and every combine.
+@pytest.mark.parametrize("T", [64, 1024])
+def test_forward_all_tokens_one_expert_set(T):
+    _say("degenerate routing", T)
+    wl = workloads.Workload(f"ties_{T}", T, 512, 16, 2, 256, "mxfp8", "mxfp8", False, 11)
+    from mx_quantized_grouped_amd.weights import ExpertLoader
+    shape = shape_of(wl)
+    loader = ExpertLoader(shape, DEV)
+    for e in range(wl.E + 1):
+        loader.add_expert(e, *workloads.draw_expert(wl, e))
+    packed = loader.finish()
+    xb = workloads.draw_x(wl)
+    lb = np.zeros((T, wl.E), dtype=np.uint16)  # bf16 +0.0 everywhere
+    ref = moe.moe_block(f64(xb), f64(lb), oracle_weights(wl), wl.top_k, wl.act_fmt)
+    assert np.array_equal(ref.ids[:, :2], np.tile([0, 1], (T, 1)))
+    for opt in [None, B.Options(1, 1, 0, 0), B.Options(1, 2, 0, 0), B.Options(2, 1, 0, 0),
+                B.Options(2, 3, 0, 0)]:
+        y = B.mxmoe_forward(shape, bf16_tensor(xb), bf16_tensor(lb), packed, options=opt)
+        torch.cuda.synchronize()
+        st = moe.parity_stats(y.float().cpu().numpy(), ref.y)
+        assert tolerance_ok(st), (opt and (opt.launcher, opt.combine), st)
+
+
 def test_forward_zero_tokens_is_noop():
     shape = B.Shape.of(0, 256, 8, 2, 128, "mxfp8")
     assert B.lib().mxmoe_forward(shape, None, None, None, None, None, None, None, None, 0,
