@@ -15,7 +15,7 @@ gate in front of it, step 0: l = x . W_g^T, [L3] "Sửa thước đo trước kh
               passage, Fig. 4: the shared expert is a table entry every token selects).
   2. align  : slots grouped expert by expert into tile-padded blocks (the layout the grouped GEMMs
               consume; [M3] local-shapes passage on grouped MoE programs).
-  3. Q1     : x[t] -> MXFP8 (E4M3), one scale per 32 along H.
+  3. Q1     : x[t] -> MXFP8 (E4M3), one scale per 32 along H (MXFP4, E2M1, for the W4A4 reading).
   4. G1     : gate/up projection of the quantised row by the (dequantised) fused W13 of the expert.
   5. S      : SwiGLU, a = SiLU(gate) * up ([M3] shared-expert passage lists "gate/up projection,
               activation, down projection" as the dense expert MLP).
@@ -206,23 +206,31 @@ def silu(g: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g))
 
 
+# Element format of the quantised activations. MXFP8 activations are the served configuration
+# ([M3] opening results). For MXFP4 weights the pages give throughput but no activation format
+# ([M3] opening results, the MXFP4 bullet); the "mxfp4" activation format reads W4A4 as the same MX
+# rule with E2M1 elements (largest exponent 2) in both Q1 and Q2.
+ACT_ELEMENT = {"mxfp8": "e4m3", "mxfp4": "e2m1"}
+
+
 def quantize_activation_rows(x: np.ndarray, act_fmt: str) -> np.ndarray:
-    """Q1: MXFP8 (E4M3) along the row, one scale per 32 values; identity for bf16."""
+    """Q1: MX along the row, one scale per 32 values (E4M3 elements for "mxfp8", E2M1 for
+    "mxfp4"); identity for bf16."""
     if act_fmt == "bf16":
         return np.asarray(x, np.float64)
-    return mx.quantize_dequantize(x, "e4m3")
+    return mx.quantize_dequantize(x, ACT_ELEMENT[act_fmt])
 
 
 def quantize_intermediate(a: np.ndarray, act_fmt: str) -> np.ndarray:
     """Q2 on the SwiGLU output, per slot row along I.
 
     Reading: the GPU path holds a in fp32 and takes its rounding decisions there, so the oracle
-    first rounds its fp64 a to fp32 and then applies the same rule as Q1 (MXFP8); in the bf16
-    workload a is rounded to bf16 before the down projection."""
+    first rounds its fp64 a to fp32 and then applies the same rule as Q1 (same element format); in
+    the bf16 workload a is rounded to bf16 before the down projection."""
     a32 = np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
     if act_fmt == "bf16":
         return mx.round_to_bf16(a32)
-    return mx.quantize_dequantize(a32, "e4m3")
+    return mx.quantize_dequantize(a32, ACT_ELEMENT[act_fmt])
 
 
 @dataclass

@@ -224,6 +224,56 @@ def test_block_matches_dense_brute_force(fmt):
     assert np.allclose(r.y, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
 
 
+def _shared_only_ones(H, I, E=2):
+    """Routed experts all zero; every shared-expert weight 1."""
+    def getter(e):
+        if e == E:
+            return np.ones((2 * I, H)), np.ones((H, I))
+        return np.zeros((2 * I, H)), np.zeros((H, I))
+    return moe.ExpertWeights(E, H, I, "mxfp8", getter)
+
+
+@pytest.mark.parametrize("act_fmt,expect", [("mxfp4", 6144.0), ("mxfp8", 7168.0)])
+def test_block_activation_format_closed_form(act_fmt, expect):
+    # H = I = 32, every x = 0.5, only the shared expert (all weights 1) contributes.
+    # Q1: amax 0.5 gives scale 2^(-1 - emax) and 0.5 lands on a grid point in both formats.
+    # gate = up = 32 * 0.5 = 16; a = SiLU(16) * 16 = 256 / (1 + e^-16), 255.99997 in fp32.
+    # Q2, E2M1 (emax 2): scale 2^(7 - 2) = 32, a / 32 = 7.99999 saturates to 6: a^ = 192.
+    # Q2, E4M3 (emax 8): scale 2^(7 - 8) = 1/2, a * 2 = 511.9999 saturates to 448: a^ = 224.
+    # down: y = 32 * a^ in every column (6144 and 7168).
+    H = I = 32
+    x = np.full((3, H), 0.5)
+    lg = np.zeros((3, 2))
+    r = moe.moe_block(x, lg, _shared_only_ones(H, I), 1, act_fmt)
+    assert np.all(r.y == expect)
+
+
+def test_mxfp4_activations_on_the_e2m1_grid():
+    # Q1 for "mxfp4": every dequantised value of a 32-block is an E2M1 value (0, 0.5, 1, 1.5, 2, 3,
+    # 4, 6 and negatives) times 2^(floor(log2 amax) - 2), with the block maximum mapped to [4, 8)
+    # before rounding (so to 4 or 6).
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((6, 128)) * np.exp2(rng.integers(-6, 6, (6, 1)))
+    q = moe.quantize_activation_rows(x, "mxfp4")
+    grid = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
+    for t in range(6):
+        for b in range(4):
+            blk, qb = x[t, 32 * b:32 * b + 32], q[t, 32 * b:32 * b + 32]
+            s = math.floor(math.log2(np.abs(blk).max())) - 2
+            assert all(abs(v) / 2.0 ** s in grid for v in qb)
+            assert np.abs(qb).max() / 2.0 ** s in (4.0, 6.0)
+    # and it is not the MXFP8 rule
+    assert not np.array_equal(q, moe.quantize_activation_rows(x, "mxfp8"))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_block_w4a4_matches_dense_brute_force(fmt):
+    w, x, lg, W = _tiny(fmt=fmt, T=3, H=64, E=4, k=2, I=32, seed=4)
+    r = moe.moe_block(x, lg, W, w.top_k, "mxfp4")
+    ref = _dense_loops(x, lg, W, w.top_k, "mxfp4")
+    assert np.allclose(r.y, ref, rtol=1e-12, atol=1e-15 * np.abs(ref).max())
+
+
 def test_shared_expert_equals_dense_mlp():
     # Routed experts with all-zero weights contribute nothing; the block must then equal the shared
     # expert run as a plain dense MLP on all tokens at once (matrix form, weight 1).
