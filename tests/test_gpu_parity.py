@@ -66,6 +66,22 @@ def test_quantize_bit_exact(fmt, src):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+@pytest.mark.parametrize("name", ["decode_mxfp4", "wide512_mxfp4_T6"])
+def test_quantize_w4a4_activations(name):
+    # The MXFP4-activation reading (W4A4): the GPU quantiser on a workload's bf16 activations,
+    # decoded, equals the oracle's activation quantisation with E2M1 elements, value for value.
+    _say("quantize w4a4 activations", name)
+    w = workloads.get(name)
+    xb = workloads.draw_x(w)
+    codes, scales = B.mxmoe_quantize(bf16_tensor(xb), "mxfp4")
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    unpacked = np.stack([c & 0xF, c >> 4], axis=-1).reshape(w.T, w.H)
+    got = mx.dequantize(unpacked, scales.cpu().numpy(), "e2m1")
+    ref = moe.quantize_activation_rows(f64(xb), "mxfp4")
+    assert np.array_equal(got, ref)
+
+
 def test_quantize_exhaustive_bf16():
     # Every finite bf16 value, in blocks of 32 shuffled together (so each block's scale varies).
     _say("quantize exhaustive bf16")
