@@ -62,37 +62,17 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
 // experts); walked in global memory, the per-thread chain of loads made this pass take 16 us for
 // an 8K-token batch.
 constexpr int kScanLdsCounts = 28 * 1024;
-__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
-                                                              int32_t* __restrict__ start,
-                                                              int32_t* __restrict__ offs,
-                                                              int nchunks, int S, int E1, int bm,
-                                                              int cap, AlignOut o) {
-  __shared__ int cnt[kAlignMaxE1];
-  __shared__ int off[kAlignMaxE1 + 1];
-  __shared__ int s_wave[kAlignWaves];
-  __shared__ int seg_sum[kAlignThreads];
-  __shared__ int hist_l[kScanLdsCounts];
+
+// The scan proper over the chunk histograms `hist` (LDS or global). It is inlined once per
+// address space: through one pointer that may be either, every read of the walks below became a
+// generic (flat) load waited on one at a time, ~70 of them per thread for 4096 tokens over 512
+// experts.
+__device__ __forceinline__ void align_scan_body(const int32_t* __restrict__ hist,
+                                                int32_t* __restrict__ start,
+                                                int32_t* __restrict__ offs, int nchunks, int S,
+                                                int E1, int bm, int cap, const AlignOut& o,
+                                                int* cnt, int* off, int* s_wave, int* seg_sum) {
   const int t = threadIdx.x;
-  const int nh = nchunks * E1;
-  const int32_t* hist = hist_g;
-  if (nh <= kScanLdsCounts) {
-    constexpr int kB = kScanLdsCounts / kAlignThreads;  // every load in one batch
-    for (int base = t; base < nh; base += kB * kAlignThreads) {
-      int v[kB];
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const int i = base + j * kAlignThreads;
-        v[j] = i < nh ? hist_g[i] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const int i = base + j * kAlignThreads;
-        if (i < nh) hist_l[i] = v[j];
-      }
-    }
-    __syncthreads();
-    hist = hist_l;
-  }
   const int P = E1 >= kAlignThreads ? 1 : kAlignThreads / E1;  // segments per expert
   const int seg = (nchunks + P - 1) / P;
   const int part = t / E1, e = t - part * E1;
@@ -106,8 +86,10 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
   for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
     if (pass == 1 && (P != 1 || ee >= E1)) break;
     int sum = 0;
-    if (mine && ee < E1)
+    if (mine && ee < E1) {
+#pragma unroll 8
       for (int c = c_lo; c < c_hi; ++c) sum += hist[(size_t)c * E1 + ee];
+    }
     if (pass == 0) seg_sum[t] = sum;
     else cnt[ee] = sum;
   }
@@ -130,10 +112,45 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
     if (pass == 1 && (P != 1 || ee >= E1)) break;
     if (!mine || ee >= E1) continue;
     int run = off[ee] + (P == 1 ? 0 : seg_sum[t]);
+#pragma unroll 8
     for (int c = c_lo; c < c_hi; ++c) {
       start[(size_t)c * E1 + ee] = run;
       run += hist[(size_t)c * E1 + ee];
     }
+  }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
+                                                              int32_t* __restrict__ start,
+                                                              int32_t* __restrict__ offs,
+                                                              int nchunks, int S, int E1, int bm,
+                                                              int cap, AlignOut o) {
+  __shared__ int cnt[kAlignMaxE1];
+  __shared__ int off[kAlignMaxE1 + 1];
+  __shared__ int s_wave[kAlignWaves];
+  __shared__ int seg_sum[kAlignThreads];
+  __shared__ int hist_l[kScanLdsCounts];
+  const int t = threadIdx.x;
+  const int nh = nchunks * E1;
+  if (nh <= kScanLdsCounts) {
+    constexpr int kB = kScanLdsCounts / kAlignThreads;  // every load in one batch
+    for (int base = t; base < nh; base += kB * kAlignThreads) {
+      int v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = base + j * kAlignThreads;
+        v[j] = i < nh ? hist_g[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = base + j * kAlignThreads;
+        if (i < nh) hist_l[i] = v[j];
+      }
+    }
+    __syncthreads();
+    align_scan_body(hist_l, start, offs, nchunks, S, E1, bm, cap, o, cnt, off, s_wave, seg_sum);
+  } else {
+    align_scan_body(hist_g, start, offs, nchunks, S, E1, bm, cap, o, cnt, off, s_wave, seg_sum);
   }
 }
 
