@@ -10,11 +10,15 @@
 // rows (the MFMA operand layout). The tile grows with the batch (measured, hidden 3072 and 128
 // experts unless stated): one fragment up to 256 tokens (the weight stream spread over the most
 // CUs: 7.1 us for 32 tokens, 7.4 us for 128, against 9.7 us with 16 x 32 tiles); 16 x 32 up to
-// 2048 tokens. Beyond, the tiles are staged through LDS (k_gate_lds: whole cache lines per load
-// instead of 64-byte row segments), 64 x 32 tiles, and 64 x 64 from 512 experts on: 8192 tokens
-// 19.6 us (26.5 us for the best register tile, 64 x 64; 56 us for 16 x 64 tiles, which re-read the
-// weights for every 16 tokens); 4096 tokens x 512 experts, hidden 2048: 19.8 us (28.8 us for the
-// best register tile, 64 x 128). Loading more K-steps ahead in the register tiles changed nothing.
+// 1024 tokens (10.1 us at 1024). Beyond, and beyond 256 tokens from 512 experts on, the tiles are
+// staged through LDS (k_gate_lds: whole cache lines per load instead of 64-byte row segments):
+// 32 x 64 up to 4096 tokens (2048 tokens: 12.0 us against 18.3 us for 16 x 32), 64 x 32 beyond
+// (8192 tokens: 19.6 us; 26.5 us for the best register tile, 64 x 64; 56 us for 16 x 64, which
+// re-reads the weights for every 16 tokens). With 512 experts, hidden 2048: 32 x 64 up to 1024
+// tokens (9.4 us against 23.7 us for 16 x 32), 64 x 64 beyond (4096 tokens: 19.8 us; 28.8 us for
+// the best register tile, 64 x 128). Loading more K-steps ahead in the register tiles changed
+// nothing. Every tile gives the same logits: wave w always takes K-steps w, w + 4, ... and the
+// partial sums are added in wave order.
 #include <cstdlib>
 
 #include "device.h"
@@ -243,7 +247,9 @@ hipError_t launch_gate_f(const uint16_t* x, const uint16_t* wg, int T, int H, in
 
 hipError_t launch_gate(const uint16_t* x, const uint16_t* wg, int T, int H, int E, bool f32,
                        void* out, hipStream_t st) {
-  int cfg = T <= 256 ? 11 : (T <= 2048 ? 12 : (E >= 512 ? 144 : 142));
+  int cfg = T <= 256 ? 11
+            : E >= 512 ? (T <= 1024 ? 124 : 144)
+                       : (T <= 1024 ? 12 : (T <= 4096 ? 124 : 142));
   // A/B knob: 10 * TM + F for register tiles, 100 + 10 * TM + F for LDS-staged ones
   if (const char* env = getenv("MXMOE_GATE_TILE")) cfg = atoi(env);
   switch (cfg) {

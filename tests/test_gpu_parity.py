@@ -123,6 +123,7 @@ def _gate_bound(xb, gb):
 
 
 @pytest.mark.parametrize("T,H,E", [(32, 3072, 128), (8192, 3072, 128), (6, 2048, 512),
+                                   (700, 160, 515), (1500, 3072, 128),
                                    (1, 2048, 512), (37, 96, 70), (100, 64, 1), (65, 128, 130),
                                    (4096, 2048, 512), (300, 256, 130), (2100, 96, 520),
                                    (3000, 64, 200)])
@@ -142,6 +143,22 @@ def test_gate_parity(T, H, E):
     assert torch.equal(l32, again)                      # fixed-order sums: reproducible
     b = l16.float().cpu().numpy().astype(np.float64)   # one more rounding, to bf16
     assert np.all(np.abs(b - ref) <= bound + 2.0 ** -8 * np.abs(ref))
+
+
+def test_gate_tiles_agree(monkeypatch):
+    # Every tile shape of the gate, register or LDS-staged, splits K over the 4 waves the same way
+    # and adds their partial sums in wave order, so the logits are bit-identical whatever tile the
+    # launcher picks for a batch size.
+    _say("gate tiles agree")
+    wl = workloads.Workload("gate_tiles", 1100, 224, 140, 1, 128, "mxfp8", "mxfp8", False, 13)
+    x, g = bf16_tensor(workloads.draw_x(wl)), bf16_tensor(workloads.draw_gate(wl))
+    outs = {}
+    for cfg in [11, 12, 14, 21, 22, 24, 28, 41, 42, 44, 48, 84, 124, 142, 144, 148]:
+        monkeypatch.setenv("MXMOE_GATE_TILE", str(cfg))
+        outs[cfg] = B.mxmoe_gate(x, g)
+    torch.cuda.synchronize()
+    for cfg, o in outs.items():
+        assert torch.equal(o, outs[11]), cfg
 
 
 def test_gate_then_route_and_forward():
