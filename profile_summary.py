@@ -15,7 +15,7 @@ runs, profiles/traffic_decode_prefill_mxfp8.md and profiles/traffic.json. bench.
 latter for its roofline `traffic` figure, keyed by the sha256 of the GEMM source the counters
 were taken on.
 
-Usage: python profile_summary.py <dir> [--traffic W=KERNEL ...]
+Usage: python profile_summary.py <dir> [--traffic W=KERNEL ...] [--out DIR (default profiles/)]
 """
 import argparse
 import glob
@@ -64,7 +64,7 @@ def kernels(db):
     return d
 
 
-def trace_md(src, wl):
+def trace_md(src, wl, out):
     d = kernels(database(os.path.join(src, f"prof_trace_{wl}")))
     lines = [f"# Kernel durations: {wl}", "", "Command (repository root on the MI355X box):", "", "```",
              TRACE_CMD.format(wl=wl), "```", "",
@@ -86,7 +86,7 @@ def trace_md(src, wl):
     lines += ["", f"Sum of the per-launch averages of the block's kernels: {tot:.1f} us per forward call.",
               "`k_gate` (and `k_gate_lds`) is the router gate in front of the block (bench.py's "
               "`gate` timing, weights in cache), not part of that sum."]
-    with open(os.path.join(ROOT, "profiles", f"kernels_{wl}.md"), "w") as f:
+    with open(os.path.join(out, f"kernels_{wl}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return d
 
@@ -104,7 +104,7 @@ def pmc(db, counter):
     return d, copies
 
 
-def traffic(src, gate_up):
+def traffic(src, gate_up, out):
     """gate_up: workload -> name of its gate_up kernel in the trace."""
     sha = hashlib.sha256(open(os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"),
                               "rb").read()).hexdigest()[:16]
@@ -137,28 +137,29 @@ def traffic(src, gate_up):
         md += ["", f"gate_up (`{gk}`): {(rb + wb) / 1e6:.1f} MB of HBM traffic per launch.", ""]
         rec[wl] = {"kernel": gk, "gemm_src_sha": sha, "bytes_per_launch": rb + wb, "read_bytes": rb,
                    "write_bytes": wb, "fetch_scale": fs, "write_scale": ws}
-    with open(os.path.join(ROOT, "profiles", "traffic_decode_prefill_mxfp8.md"), "w") as f:
+    with open(os.path.join(out, "traffic_decode_prefill_mxfp8.md"), "w") as f:
         f.write("\n".join(md))
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(os.path.join(out, "traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     return rec
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("src", help="directory with the prof_trace_* / prof_pmc_* run outputs")
     ap.add_argument("--traffic", nargs="*", default=[
         "decode_mxfp8=k_gemm_stream<0, 1, true, 3, 1, 2>",
         "prefill_mxfp8=k_gemm_tile<0, true, true, true>"],
         help="WORKLOAD=gate_up kernel name, for the counter summary")
-    a = ap.parse_args()
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args(argv)
     for d in sorted(glob.glob(os.path.join(a.src, "prof_trace_*"))):
         if os.path.isdir(d):
             wl = os.path.basename(d)[len("prof_trace_"):]
-            t = trace_md(a.src, wl)
+            t = trace_md(a.src, wl, a.out)
             print(wl, {k: round(float(np.mean(v["dur"])), 2) for k, v in t.items()})
     if a.traffic:
-        print(json.dumps(traffic(a.src, dict(x.split("=", 1) for x in a.traffic)), indent=1))
+        print(json.dumps(traffic(a.src, dict(x.split("=", 1) for x in a.traffic), a.out), indent=1))
 
 
 if __name__ == "__main__":
