@@ -222,15 +222,16 @@ def quantize_activation_rows(x: np.ndarray, act_fmt: str) -> np.ndarray:
 
 
 def quantize_intermediate(a: np.ndarray, act_fmt: str) -> np.ndarray:
-    """Q2 on the SwiGLU output, per slot row along I.
-
-    Reading: the GPU path holds a in fp32 and takes its rounding decisions there, so the oracle
-    first rounds its fp64 a to fp32 and then applies the same rule as Q1 (same element format); in
-    the bf16 workload a is rounded to bf16 before the down projection."""
-    a32 = np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+    """Q2 on the SwiGLU output, per slot row along I: the MX rule of Q1 (same element format)
+    applied to the exact a; in the unquantised workload a is rounded to bf16 before the down
+    projection. The dense expert MLP sequence of [M3]'s shared-expert passage stores the activation
+    output between the two projections; the MX format of that store is the served format ([M3]
+    opening results), so the rule applies to a as the activation defines it, with no intermediate
+    precision in between."""
+    a = np.asarray(a, np.float64)
     if act_fmt == "bf16":
-        return mx.round_to_bf16(a32)
-    return mx.quantize_dequantize(a32, ACT_ELEMENT[act_fmt])
+        return mx.round_to_bf16(a)
+    return mx.quantize_dequantize(a, ACT_ELEMENT[act_fmt])
 
 
 @dataclass
@@ -243,14 +244,18 @@ class BlockResult:
 
 
 def moe_block(x: np.ndarray, logits: np.ndarray, weights: ExpertWeights, top_k: int,
-              act_fmt: str, tokens=None) -> BlockResult:
+              act_fmt: str, tokens=None, keep_intermediate: bool = False) -> BlockResult:
     """The whole block for the requested tokens (default: all), grouped by expert.
 
     x: [T, H] bf16 values (fp64), logits: [T, E]. For each expert e in ascending order the slots
     routed to it form one group ([M3] Fig. 4: routed and shared experts share one grouped-GEMM
     pass); their quantised rows are multiplied by the dequantised W13 of e (one fp64 matmul), SiLU(
     gate) * up is quantised per row (Q2), multiplied by W2 of e, and added into y[t] with the
-    routing weight of the slot (weight applied after the down projection, in the combine)."""
+    routing weight of the slot (weight applied after the down projection, in the combine).
+
+    keep_intermediate: also return, in extras["intermediate"], each computed slot's Q2 result as
+    {(t, j): (codes, scale bytes)} for MX activations (the MX quantiser's own output for the row)
+    or {(t, j): bf16 values} for the unquantised workload."""
     x = np.asarray(x, np.float64)
     T, H = x.shape
     ids, w = route(logits, top_k)
@@ -260,8 +265,8 @@ def moe_block(x: np.ndarray, logits: np.ndarray, weights: ExpertWeights, top_k: 
         tokens = np.arange(T)
     tokens = np.asarray(tokens, dtype=np.int64)
     xq = quantize_activation_rows(x[tokens], act_fmt)          # Q1 on the requested rows only
-    row_of = {int(t): r for r, t in enumerate(tokens)}
     y = np.zeros((T, H), dtype=np.float64)
+    inter = {}
     sub_ids = ids[tokens]
     for e in range(E + 1):
         rr, jj = np.nonzero(sub_ids == e)                        # slots (token row, j) on expert e
@@ -276,7 +281,13 @@ def moe_block(x: np.ndarray, logits: np.ndarray, weights: ExpertWeights, top_k: 
         d = ah @ w2.T                                            # G2: [n_e, H]
         wt = w[tokens[rr], jj]
         np.add.at(y, tokens[rr], wt[:, None] * d)                # combine
-    return BlockResult(y=y, ids=ids, weights=w, tokens=tokens)
+        if keep_intermediate:
+            coded = (None if act_fmt == "bf16" else mx.quantize(a, ACT_ELEMENT[act_fmt]))
+            for i, (r_, j_) in enumerate(zip(rr, jj)):
+                key = (int(tokens[r_]), int(j_))
+                inter[key] = ah[i] if coded is None else (coded[0][i], coded[1][i])
+    return BlockResult(y=y, ids=ids, weights=w, tokens=tokens,
+                       extras={"intermediate": inter} if keep_intermediate else {})
 
 
 # ---------------------------------------------------------------- pass/fail measure

@@ -138,11 +138,13 @@ def quantize_dequantize(x: np.ndarray, fmt: str) -> np.ndarray:
     return dequantize(c, s, fmt)
 
 
-# ---------------------------------------------------------------- bf16 storage rounding
+# ---------------------------------------------------------------- bf16 rounding
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
-    """Nearest bf16 value (ties to even) of fp64 inputs, returned as fp64. Values are first rounded
-    to fp32, the precision the GPU path holds them in before its own bf16 rounding."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+    """Nearest bf16 value (ties to even) of each fp64 input, returned as fp64, rounded once and
+    directly from the exact value. bf16 keeps 8 significant bits: for |x| in [2^(e-1), 2^e) the
+    grid step is 2^(e-8), and below the smallest normal (2^-126) the step stays 2^-133. Finite
+    inputs within the bf16 range."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                               # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.maximum(e.astype(np.int64), -125) - 8     # exponent of the grid step
+    return np.ldexp(np.rint(np.ldexp(x, -q)), q)     # np.rint: nearest, ties to even

@@ -290,7 +290,7 @@ def test_shared_expert_equals_dense_mlp():
     G = xq @ w13s[:w.I].T
     U = xq @ w13s[w.I:].T
     A = (G / (1 + np.exp(-G))) * U
-    Ah = mx.quantize_dequantize(A.astype(np.float32).astype(np.float64), "e4m3")
+    Ah = mx.quantize_dequantize(A, "e4m3")
     Y = Ah @ w2s.T
     assert np.allclose(r.y, Y, rtol=1e-13, atol=1e-16)
 
@@ -305,9 +305,94 @@ def test_single_expert_is_dense_swiglu_mlp():
     for e in (0, 1):
         w13, w2 = W(e)
         G, U = xq @ w13[:32].T, xq @ w13[32:].T
-        y += mx.quantize_dequantize(((G / (1 + np.exp(-G))) * U).astype(np.float32).astype(
-            np.float64), "e4m3") @ w2.T
+        y += mx.quantize_dequantize((G / (1 + np.exp(-G))) * U, "e4m3") @ w2.T
     assert np.allclose(r.y, y, rtol=1e-13, atol=1e-16)
+
+
+def test_q2_quantises_the_exact_swiglu_output():
+    # Hand-worked block: amax 300 gives the shared exponent floor(log2 300) - 8 = 0, so the second
+    # element is rounded on the E4M3 grid of [1, 2) (step 1/8). 1.0625 + 2^-40 lies just above the
+    # midpoint of 1 and 1.125 and must round up to 1.125 (code 0x39); held in fp32 first it would
+    # be exactly 1.0625, a tie, and go to the even code 0x38 (1.0).
+    a = np.zeros((1, 32))
+    a[0, 0], a[0, 1] = 300.0, 1.0625 + 2.0 ** -40
+    q = moe.quantize_intermediate(a, "mxfp8")
+    assert q[0, 1] == 1.125 and q[0, 0] == 288.0          # 300 -> grid step 32 in [256, 512)
+    # the bf16 workload: one rounding of the exact value (1 + 2^-8 + 2^-30 -> 1 + 2^-7)
+    b = np.array([[1.0 + 2.0 ** -8 + 2.0 ** -30]])
+    assert moe.quantize_intermediate(b, "bf16")[0, 0] == 1.0 + 2.0 ** -7
+
+
+def test_keep_intermediate_reports_q2_codes():
+    w, x, lg, W = _tiny(T=3, H=64, E=4, k=2, I=64)
+    r = moe.moe_block(x, lg, W, w.top_k, w.act_fmt, keep_intermediate=True)
+    inter = r.extras["intermediate"]
+    assert sorted(inter) == [(t, j) for t in range(3) for j in range(3)]
+    xq = moe.quantize_activation_rows(x, "mxfp8")
+    for (t, j), (codes, scales) in inter.items():
+        w13, _ = W(int(r.ids[t, j]))
+        g, u = xq[t] @ w13[:w.I].T, xq[t] @ w13[w.I:].T
+        a = g / (1 + np.exp(-g)) * u
+        assert np.array_equal(mx.dequantize(codes, scales, "e4m3"), moe.quantize_intermediate(a[None], "mxfp8")[0])
+
+
+# ---------------------------------------------------------------- expert weights from draws
+def _from_draws_explicit(a, b, el):
+    """Quantisation of one expert's fp32 draws written out row by row: every row of W13 [2I, H]
+    is cut into 32-element blocks along H, every row of W2 [H, I] along I, and each block is
+    decoded as code value * 2^(byte - 127)."""
+    def rows(m):
+        out = np.empty(m.shape)
+        for r in range(m.shape[0]):
+            for c0 in range(0, m.shape[1], 32):
+                codes, sb = mx.quantize(m[r, c0:c0 + 32][None], el)
+                out[r, c0:c0 + 32] = mx.decode(codes[0], el) * 2.0 ** (int(sb[0, 0]) - 127)
+        return out
+    return rows(np.asarray(a, np.float64)), rows(np.asarray(b, np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_from_draws_quantises_along_k(fmt):
+    # H != I, so blocks along the wrong axis would not even line up with the matrix shape.
+    w = workloads.Workload("fd", 2, 96, 3, 2, 64, fmt, "mxfp8", False, 6)
+    W = moe.ExpertWeights.from_draws(lambda e: workloads.draw_expert(w, e), w.E, w.H, w.I, fmt)
+    el = {"mxfp8": "e4m3", "mxfp4": "e2m1"}[fmt]
+    for e in range(w.E + 1):
+        a, b = workloads.draw_expert(w, e)
+        w13, w2 = W(e)
+        assert w13.shape == (2 * w.I, w.H) and w2.shape == (w.H, w.I)
+        ra, rb = _from_draws_explicit(a, b, el)
+        assert np.array_equal(w13, ra) and np.array_equal(w2, rb)
+        # and through from_mx on codes quantised along H (W13) and along I (W2)
+        c13, s13 = mx.quantize(a.astype(np.float64), el)
+        c2, s2 = mx.quantize(b.astype(np.float64), el)
+        assert s13.shape == (2 * w.I, w.H // 32) and s2.shape == (w.H, w.I // 32)
+        Wm = moe.ExpertWeights.from_mx(c13[None], s13[None], c2[None], s2[None], fmt)
+        m13, m2 = Wm(0)
+        assert np.array_equal(m13, w13) and np.array_equal(m2, w2)
+
+
+def test_from_draws_axis_hand_worked():
+    # W13 [2I = 64, H = 64], W2 [H = 64, I = 32]. Element (0, 0) of W13 is 0.011 and (0, 1) is 400:
+    # along H its block has amax 400, shared exponent 0 (byte 127), and 0.011 falls in the
+    # subnormal E4M3 range: 0.011 / 2^-9 = 5.63 -> 6 * 2^-9 = 0.01171875. Along the other axis its
+    # block (column 0, rows 0..31) would have amax 0.011, shared exponent -7 - 8 = -15 (byte 112):
+    # 0.011 * 2^15 = 360.4 -> 352 (grid step 32) -> 0.0107421875. W2 gets the same pair at (0, 0),
+    # (0, 1), so its blocks run along I.
+    w13 = np.zeros((64, 64), np.float32)
+    w13[0, 0], w13[0, 1] = 0.011, 400.0
+    w2 = np.zeros((64, 32), np.float32)
+    w2[0, 0], w2[0, 1] = 0.011, 400.0
+    W = moe.ExpertWeights.from_draws(lambda e: (w13, w2), 0, 64, 32, "mxfp8")
+    a, b = W(0)
+    assert a[0, 0] == 0.01171875 and b[0, 0] == 0.01171875
+    # 400 is the midpoint of 384 and 416 (grid step 32 in [256, 512)): ties go to the even code
+    assert a[0, 1] == 384.0 and b[0, 1] == 384.0
+    # the scale bytes of those blocks
+    _, s = mx.quantize(w13.astype(np.float64), "e4m3")
+    assert s[0, 0] == 127
+    _, sw = mx.quantize(w13.T.astype(np.float64), "e4m3")
+    assert sw[0, 0] == 112                                   # the wrong axis: another byte
 
 
 def test_token_permutation_invariance():

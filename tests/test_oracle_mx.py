@@ -144,10 +144,40 @@ def test_all_bf16_values_quantise_within_half_ulp():
 
 
 def test_round_to_bf16_matches_torch():
+    # On fp32 inputs a single rounding to bf16 is what torch's fp32 -> bf16 cast does (RNE).
     rng = np.random.default_rng(3)
     x = rng.standard_normal(100000) * np.exp(rng.uniform(-30, 30, size=100000))
-    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    assert np.array_equal(mx.round_to_bf16(x), ref)
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(mx.round_to_bf16(x32.astype(np.float64)), ref)
+
+
+def test_round_to_bf16_is_one_rounding_of_the_exact_value():
+    # Hand-worked: 1 + 2^-8 + 2^-30 lies just above the midpoint between the bf16 neighbours 1 and
+    # 1 + 2^-7, so it rounds up. Rounding to fp32 first would land exactly on the midpoint
+    # (2^-30 is below half an fp32 ulp at 1) and the tie would go to the even neighbour, 1.
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert mx.round_to_bf16(np.array([v]))[0] == 1.0 + 2.0 ** -7
+    assert mx.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0          # exact tie: even
+    assert mx.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert mx.round_to_bf16(np.array([-(1.0 + 2.0 ** -8 + 2.0 ** -30)]))[0] == -(1.0 + 2.0 ** -7)
+    # below the smallest normal (2^-126) the grid step stays 2^-133
+    assert mx.round_to_bf16(np.array([2.0 ** -133 * 1.5]))[0] == 2.0 ** -132
+    assert mx.round_to_bf16(np.array([2.0 ** -130 + 2.0 ** -134]))[0] == 2.0 ** -130
+
+
+def test_round_to_bf16_against_bit_formula():
+    # Independent form: the bf16 neighbours of v are the fp64 values whose low 45 mantissa bits are
+    # zero; the nearest one (ties to the even 8-bit significand) is chosen by comparing distances.
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, size=20000))
+    u = v.view(np.uint64)
+    lo = (u & ~np.uint64((1 << 45) - 1)).view(np.float64)             # toward zero
+    hi = ((u | np.uint64((1 << 45) - 1)) + np.uint64(1)).view(np.float64)  # away from zero
+    d_lo, d_hi = np.abs(v - lo), np.abs(hi - v)
+    lo_even = ((lo.view(np.uint64) >> np.uint64(45)) & np.uint64(1)) == 0
+    want = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo_even, lo, hi)))
+    assert np.array_equal(mx.round_to_bf16(v), want)
 
 
 def test_dequantize_inverts_scale_layout():
