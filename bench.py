@@ -12,8 +12,8 @@ decode M; per-workload TFLOP/s, GB/s and roofline fractions (decode and prefill 
 `workloads`. `roofline` is for the dominant kernel (gate_up), timed with HIP events that the
 library records on its own stream at stage boundaries. `cpu_baseline` is the fp64 CPU oracle on a
 bounded sample of the headline workload (host cores of the same machine). `gate` times the router
-gate in front of the block (mxmoe_gate, x . W_g^T to fp32 logits) on each workload's shapes, its
-weights in cache between back-to-back calls."""
+gate in front of the block (mxmoe_gate, x . W_g^T to fp32 logits) on each workload's shapes, warm
+(back-to-back calls) and cold (caches flushed before each call)."""
 from __future__ import annotations
 
 import argparse
@@ -248,9 +248,14 @@ def measure(name, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def measure_gate(name, steps=100):
+def measure_gate(name, steps=100, cold_reps=30):
     """Router gate (mxmoe_gate, fp32 logits) on the workload's x [T, H] and a seeded bf16 gate
-    [E, H], launched back to back (its weights stay in cache between calls)."""
+    [E, H]. Warm: launched back to back, its weights and activations staying in cache between
+    calls. Cold: before each call a 512 MiB buffer is written (more than the 256 MB memory-side
+    cache plus the eight 4 MB L2s), so x and the gate weights come from HBM, as between two layers
+    of a serving step ("Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell",
+    "Sửa thước đo trước khi sửa máy": 7 us hot against 11 us cold there); one event pair around
+    each call, reported as the median, with the median of an empty pair for the events' own cost."""
     import torch
     import workloads
     from mx_quantized_grouped_amd import binding as B
@@ -268,9 +273,25 @@ def measure_gate(name, steps=100):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold, empty = [], []
+    for i in range(cold_reps):
+        for timed in (True, False):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if timed:
+                B.mxmoe_gate(x, gw, logits=out)
+            b.record()
+            torch.cuda.synchronize()
+            (cold if timed else empty).append(a.elapsed_time(b) * 1e3)
+    del flush
     nbytes = 2 * w.T * w.H + 2 * w.E * w.H + 4 * w.T * w.E
+    cold_us = float(np.median(cold))
     return {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9,
-            "TFLOPs": 2.0 * w.T * w.H * w.E / (us * 1e-6) / 1e12, "weights": "in cache"}
+            "TFLOPs": 2.0 * w.T * w.H * w.E / (us * 1e-6) / 1e12, "weights": "in cache",
+            "cold_us": cold_us, "cold_GBps": nbytes / (cold_us * 1e-6) / 1e9,
+            "cold_event_pair_us": float(np.median(empty)), "bytes": nbytes}
 
 
 def cpu_baseline(g, n_tokens, min_seconds=10.0):
@@ -343,7 +364,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_mxfp8")
-    ap.add_argument("--extra", default="prefill_mxfp8,wide512_mxfp4_T1,wide512_mxfp4_T6",
+    ap.add_argument("--extra", default="prefill_mxfp8,decode_mxfp4,wide512_mxfp4_T1,"
+                                       "wide512_mxfp4_T6,wide512_mxfp4_T4096",
                     help="comma-separated extra workloads, 'all', or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -67,7 +67,10 @@ enum { MXMOE_COMBINE_AUTO = 0, MXMOE_COMBINE_SLOTS = 1, MXMOE_COMBINE_ATOMIC = 2
 
 /* Problem shape. Requirements: T >= 0; H % 128 == 0; I % 32 == 0; 1 <= top_k <= E <= 1024;
    w_fmt in {BF16, MXFP8_E4M3, MXFP4_E2M1}; act_fmt = MXFP8_E4M3 for MX weights and BF16 for bf16
-   weights; logits_dtype in {BF16, F32}. */
+   weights; logits_dtype in {BF16, F32}. The kernels address each of these with 32-bit offsets, so
+   each must stay below 2 GiB, or the call returns MXMOE_EUNSUPPORTED: one expert's W13 codes,
+   the activation codes (T*H bytes, 2*T*H for bf16) and the intermediate (about
+   T*(top_k+1)*I bytes plus tile padding, twice that for bf16). */
 typedef struct {
   int32_t T, H, E, top_k, I;
   int32_t w_fmt, act_fmt, logits_dtype;
@@ -78,7 +81,11 @@ typedef struct {
   int32_t launcher; /* MXMOE_LAUNCH_* */
   int32_t combine;  /* MXMOE_COMBINE_* */
   int32_t block_m;  /* align tile height (16, 32, 64, 128, 256); 0 = the launcher's default */
-  int32_t reserved; /* must be 0 */
+  /* Large-M unit order over the 8 XCDs (workgroups go round-robin over them): each XCD takes runs
+     of unit_run consecutive output tiles in turn. 0 = the launcher's default (runs of 4 row
+     tiles with all their column chunks), -1 = one contiguous range per XCD, 1 = plain linear
+     order. Only which workgroup computes which tile changes: outputs are bit-identical. */
+  int32_t unit_run;
   /* Optional array of MXMOE_STAGE_EVENTS caller-created hipEvent_t (passed as void*), recorded on
      the stream at the stage boundaries of mxmoe_forward_ex: before the prologue (routing, sort and
      activation quantisation), before gate_up, before down, before the final bf16 rounding, and
@@ -103,6 +110,13 @@ const char* mxmoe_status_string(int status);
  * HIP call; the caller owns every buffer. */
 int mxmoe_gate(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
                void* logits, void* stream);
+/* mxmoe_gate with an explicit tile (for tests and A/B runs): 0 = chosen by shape; register tiles
+ * 10*TM + F (TM 16-row token groups per wave, F 16-column expert groups: 11, 12, 14, 21, 22, 24,
+ * 28, 41, 42, 44, 48, 84) or LDS-staged tiles 100 + 10*TM + F (124, 142, 144, 148). Every tile
+ * splits the sum over H the same way, so the logits are bit-identical whatever the tile; another
+ * value returns MXMOE_EINVAL. */
+int mxmoe_gate_ex(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
+                  int tile, void* logits, void* stream);
 
 /* --------------------------------------------------------------------------------- route
  * Top-k routing with the fixed lowest-index tie-break.
@@ -176,12 +190,17 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
                      void* stream);
 
 /* Host: where forward keeps an intermediate inside its workspace, for inspection after the call
- * (routing table, sorted layout, quantised activations). which: 0 topk_ids, 1 topk_w,
- * 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off, 6 activation codes [T, H] (E4M3,
- * MX weights only; size 0 otherwise), 7 activation scale bytes [T, srs] with srs = H/32 rounded up
- * to a multiple of 16 (K-block order, padding bytes unspecified). Returns the byte offset and
- * writes the byte size to *bytes; the tile height forward used is written to *block_m. Returns
- * (size_t)-1 for an invalid request. */
+ * (routing table, sorted layout, quantised activations, quantised SwiGLU output). which:
+ * 0 topk_ids, 1 topk_w, 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off,
+ * 6 activation codes [T, H] (E4M3, MX weights only; size 0 otherwise), 7 activation scale bytes
+ * [T, srs] with srs = H/32 rounded up to a multiple of 16 (K-block order, padding bytes
+ * unspecified), 8 intermediate rows [cap, Ip] in the sorted layout's row order (row r belongs to
+ * slot sorted_ids[r]; Ip = I rounded up to a multiple of 128; E4M3 codes for MX weights, bf16
+ * values for bf16 weights), 9 intermediate scale bytes [cap, srs_I] (K-block order, srs_I = Ip/32
+ * rounded up to a multiple of 16; MX weights only). Rows of padding slots and columns past I are
+ * unspecified. Returns the byte offset and writes the byte size to *bytes; the tile height forward
+ * used is written to *block_m. Returns (size_t)-1 for an invalid request. */
+#define MXMOE_VIEW_COUNT 10
 size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int which,
                             size_t* bytes, int* block_m);
 

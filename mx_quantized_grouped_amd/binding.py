@@ -19,13 +19,13 @@ MXMOE_BF16, MXMOE_F32, MXMOE_MXFP8_E4M3, MXMOE_MXFP4_E2M1 = 0, 1, 2, 3
 MXMOE_LAUNCH_AUTO, MXMOE_LAUNCH_SMALL_M, MXMOE_LAUNCH_LARGE_M = 0, 1, 2
 MXMOE_COMBINE_AUTO, MXMOE_COMBINE_SLOTS, MXMOE_COMBINE_ATOMIC, MXMOE_COMBINE_SLOTS_BF16 = 0, 1, 2, 3
 (VIEW_TOPK_IDS, VIEW_TOPK_W, VIEW_SORTED_IDS, VIEW_BLOCK_EXPERT, VIEW_NUM_POST_PAD, VIEW_EXPERT_OFF,
- VIEW_XQ, VIEW_XS) = range(8)
+ VIEW_XQ, VIEW_XS, VIEW_H, VIEW_HS) = range(10)
 
 FMT_BY_NAME = {"bf16": MXMOE_BF16, "f32": MXMOE_F32, "mxfp8": MXMOE_MXFP8_E4M3,
                "mxfp4": MXMOE_MXFP4_E2M1}
 
 EXPORTS = [
-    "mxmoe_status_string", "mxmoe_gate", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
+    "mxmoe_status_string", "mxmoe_gate", "mxmoe_gate_ex", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
     "mxmoe_align", "mxmoe_quantize", "mxmoe_prepacked_bytes", "mxmoe_prepack",
     "mxmoe_workspace_bytes", "mxmoe_workspace_bytes_ex", "mxmoe_forward", "mxmoe_forward_ex",
     "mxmoe_workspace_view",
@@ -55,7 +55,7 @@ STAGES = ("prologue", "gate_up", "down", "finalize")
 
 class Options(ctypes.Structure):
     _fields_ = [("launcher", ctypes.c_int32), ("combine", ctypes.c_int32),
-                ("block_m", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("unit_run", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "mxmoe_status_string": (ctypes.c_char_p, [i32]),
         "mxmoe_gate": (i32, [vp, vp, i32, i32, i32, i32, vp, vp]),
+        "mxmoe_gate_ex": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp]),
         "mxmoe_route": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
         "mxmoe_align_capacity": (sz, [i32, i32, i32, i32]),
         "mxmoe_align_workspace_bytes": (sz, [i32, i32, i32, i32]),
@@ -133,15 +134,20 @@ def mxmoe_status_string(status: int) -> str:
 
 
 def mxmoe_gate(x: torch.Tensor, w_gate: torch.Tensor, out_dtype=torch.float32, logits=None,
-               stream=None):
-    """Router logits x . w_gate^T (bf16 operands, fp32 sums) as a [T, E] fp32 or bf16 tensor."""
+               stream=None, tile: int = 0):
+    """Router logits x . w_gate^T (bf16 operands, fp32 sums) as a [T, E] fp32 or bf16 tensor.
+    tile != 0 picks the kernel tile (mxmoe_gate_ex)."""
     T, H = x.shape
     E = w_gate.shape[0]
     if logits is None:
         logits = torch.empty((T, E), dtype=out_dtype, device=_dev(x))
     ld = MXMOE_F32 if logits.dtype == torch.float32 else MXMOE_BF16
-    _check(lib().mxmoe_gate(_ptr(x), _ptr(w_gate), T, H, E, ld, _ptr(logits), _stream(stream)),
-           "mxmoe_gate")
+    if tile:
+        st = lib().mxmoe_gate_ex(_ptr(x), _ptr(w_gate), T, H, E, ld, tile, _ptr(logits),
+                                 _stream(stream))
+    else:
+        st = lib().mxmoe_gate(_ptr(x), _ptr(w_gate), T, H, E, ld, _ptr(logits), _stream(stream))
+    _check(st, "mxmoe_gate")
     return logits
 
 

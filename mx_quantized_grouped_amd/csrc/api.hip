@@ -10,6 +10,36 @@
 
 using namespace mxmoe;
 
+namespace mxmoe {
+
+namespace {
+int env_int(const char* name, int unset) {
+  const char* v = getenv(name);
+  return v && *v ? atoi(v) : unset;
+}
+Tuning read_tuning() {
+  Tuning t;
+  t.trace = env_int("MXMOE_TRACE", 0) != 0;
+  t.w_nt = env_int("MXMOE_W_NT", -1);
+  t.xcd_order = env_int("MXMOE_XCD_ORDER", -1);
+  t.xcd_run_gu = env_int("MXMOE_XCD_RUN_GU", -1);
+  t.xcd_run_dn = env_int("MXMOE_XCD_RUN_DN", -1);
+  t.stream_depth = env_int("MXMOE_STREAM_DEPTH", -1);
+  t.prio = env_int("MXMOE_PRIO", -1);
+  t.tile_pipe = env_int("MXMOE_TILE_PIPE", -1);
+  t.final_nt = env_int("MXMOE_NT", -1);
+  t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
+  return t;
+}
+}  // namespace
+
+const Tuning& tuning() {
+  static const Tuning t = read_tuning();  // once per process
+  return t;
+}
+
+}  // namespace mxmoe
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -56,6 +86,9 @@ int check_shape(const mxmoe_shape* s) {
   if (!mxw && s->w_fmt != MXMOE_BF16) return MXMOE_EINVAL;
   if (mxw && s->act_fmt != MXMOE_MXFP8_E4M3) return MXMOE_EUNSUPPORTED;
   if (!mxw && s->act_fmt != MXMOE_BF16) return MXMOE_EUNSUPPORTED;
+  // one expert's prepacked W13 (W2 is half of it) is addressed with 32-bit offsets
+  const double eb = s->w_fmt == MXMOE_MXFP8_E4M3 ? 1.0 : (s->w_fmt == MXMOE_MXFP4_E2M1 ? 0.5 : 2.0);
+  if ((double)2 * s->I * s->H * eb >= (double)kMaxBufferBytes) return MXMOE_EUNSUPPORTED;
   return MXMOE_OK;
 }
 
@@ -71,14 +104,27 @@ struct Plan {
   int combine;  // 1 slots, 2 atomic, 3 bf16 slots
   bool fuse_final;  // final bf16 rounding inside the down pass (small M, atomic combine)
   int bm, cap, Ip, srs_H, srs_I;
+  int unit_run;  // large-M unit order from the options (0 = the launcher's default)
   size_t off[NSEG + 1];
 };
+
+// Every buffer the kernels address with 32-bit offsets stays below 2 GiB: activation codes and
+// scales, the intermediate and its scales, and one expert's prepacked weights (the descriptors'
+// range and the row offsets are 32-bit; the out-of-range sentinel 0x80000000 must not be valid).
+bool within_offsets(const mxmoe_shape* s, int T, int cap, int Ip, int srs_H, int srs_I, bool mx) {
+  const size_t lim = kMaxBufferBytes;
+  if ((size_t)T * s->H * (mx ? 1 : 2) >= lim) return false;
+  if ((size_t)T * srs_H >= lim) return false;
+  if ((size_t)cap * Ip * (mx ? 1 : 2) >= lim) return false;
+  if ((size_t)cap * srs_I >= lim) return false;
+  return true;
+}
 
 int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   int rc = check_shape(s);
   if (rc) return rc;
   mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr};
-  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.reserved)
+  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.unit_run < -1)
     return MXMOE_EINVAL;
   if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
   Plan& p = *P;
@@ -101,6 +147,8 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.Ip = round_up(p.I, KSTEP);
   p.srs_H = scale_row_bytes(p.H);
   p.srs_I = scale_row_bytes(p.Ip);
+  p.unit_run = o.unit_run;
+  if (!within_offsets(s, p.T, p.cap, p.Ip, p.srs_H, p.srs_I, p.mx)) return MXMOE_EUNSUPPORTED;
   size_t sz[NSEG];
   sz[SEG_IDS] = (size_t)p.S * 4;
   sz[SEG_W] = (size_t)p.S * 4;
@@ -146,7 +194,14 @@ const char* mxmoe_status_string(int status) {
 
 int mxmoe_gate(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
                void* logits, void* stream) {
+  return mxmoe_gate_ex(x, w_gate, T, H, E, logits_dtype, 0, logits, stream);
+}
+
+int mxmoe_gate_ex(const void* x, const void* w_gate, int T, int H, int E, int logits_dtype,
+                  int tile, void* logits, void* stream) {
   if (T < 0 || H <= 0 || H % 32 || E < 1 || E > kMaxExperts) return MXMOE_EINVAL;
+  if (tile != 0 && !valid_gate_tile(tile)) return MXMOE_EINVAL;
+  if ((size_t)T * H * 2 >= kMaxBufferBytes) return MXMOE_EUNSUPPORTED;
   if ((size_t)64 * H * 2 > 0x7FFFFFFFu) return MXMOE_EINVAL;  // tile offsets stay below 2^31
   if (logits_dtype != MXMOE_BF16 && logits_dtype != MXMOE_F32) return MXMOE_EINVAL;
   if (T == 0) return MXMOE_OK;
@@ -154,7 +209,7 @@ int mxmoe_gate(const void* x, const void* w_gate, int T, int H, int E, int logit
   if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(logits, logits_dtype == MXMOE_F32 ? 4 : 2))
     return MXMOE_EINVAL;
   return hip_status(launch_gate((const uint16_t*)x, (const uint16_t*)w_gate, T, H, E,
-                                logits_dtype == MXMOE_F32, logits, (hipStream_t)stream));
+                                logits_dtype == MXMOE_F32, logits, tile, (hipStream_t)stream));
 }
 
 int mxmoe_route(const void* logits, int T, int E, int top_k, int logits_dtype, int32_t* topk_ids,
@@ -255,12 +310,13 @@ size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int 
                             size_t* bytes, int* block_m) {
   Plan p;
   if (make_plan(s, opt, &p)) return (size_t)-1;
-  static const int segs[8] = {SEG_IDS,      SEG_W,      SEG_SORTED, SEG_BLOCKEXP,
-                              SEG_COUNTERS, SEG_EXPOFF, SEG_XQ,     SEG_XS};
-  if (which < 0 || which > 7) return (size_t)-1;
-  size_t sz[8] = {(size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4,
-                  (size_t)(p.cap / p.bm) * 4, 4, (size_t)(p.E1 + 1) * 4,
-                  p.mx ? (size_t)p.T * p.H : 0, p.mx ? (size_t)p.T * p.srs_H : 0};
+  static const int segs[MXMOE_VIEW_COUNT] = {SEG_IDS, SEG_W,  SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS,
+                                             SEG_EXPOFF, SEG_XQ, SEG_XS, SEG_H, SEG_HS};
+  if (which < 0 || which >= MXMOE_VIEW_COUNT) return (size_t)-1;
+  const size_t sz[MXMOE_VIEW_COUNT] = {
+      (size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4, (size_t)(p.cap / p.bm) * 4, 4,
+      (size_t)(p.E1 + 1) * 4, p.mx ? (size_t)p.T * p.H : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
+      (size_t)p.cap * p.Ip * (p.mx ? 1 : 2), p.mx ? (size_t)p.cap * p.srs_I : 0};
   if (bytes) *bytes = sz[which];
   if (block_m) *block_m = p.bm;
   return p.off[segs[which]];
@@ -300,7 +356,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   float* sorted_w = (float*)(ws + P.off[SEG_SORTW]);
   const bool slots = P.combine != MXMOE_COMBINE_ATOMIC;
 
-  if (getenv("MXMOE_TRACE"))
+  const Tuning& tn = tuning();
+  if (tn.trace)
     fprintf(stderr, "mxmoe_forward: T=%d H=%d E=%d k=%d I=%d w=%d launcher=%s block_m=%d combine=%s\n",
             P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.large ? "large_m" : "small_m", P.bm,
             P.combine == 1 ? "slots" : (P.combine == 2 ? "atomic" : "slots_bf16"));
@@ -352,10 +409,12 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.out32 = out32;
   g.combine = P.combine;
   g.T = P.T;
-  g.xcd_order = 1;
-  g.w_nt = 1;
-  if (const char* env = getenv("MXMOE_W_NT")) g.w_nt = atoi(env) != 0;  // A/B knob
-  if (const char* env = getenv("MXMOE_XCD_ORDER")) g.xcd_order = atoi(env) != 0;  // A/B knob
+  g.xcd_order = tn.xcd_order >= 0 ? tn.xcd_order != 0 : 1;
+  g.w_nt = tn.w_nt >= 0 ? tn.w_nt != 0 : 1;
+  // large-M unit order: the options' run (-1: one contiguous range per XCD), else the A/B switch,
+  // else the default runs of 4 tiles
+  auto unit_run = [&](int deflt, int env) { return P.unit_run ? (P.unit_run < 0 ? 0 : P.unit_run)
+                                                              : (env >= 0 ? env : deflt); };
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     GemmParams gu = g;
@@ -370,8 +429,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
     // large-M unit order: runs of 4 tiles (all their 256-column chunks) per XCD turn
-    gu.xcd_run = P.I >= 128 ? 4 * (P.I / 128) : 1;
-    if (const char* env = getenv("MXMOE_XCD_RUN_GU")) gu.xcd_run = atoi(env);  // A/B knob
+    gu.xcd_run = unit_run(P.I >= 128 ? 4 * (P.I / 128) : 1, tn.xcd_run_gu);
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);
@@ -385,8 +443,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.as_bytes = (uint32_t)((size_t)P.cap * P.srs_I);
     dn.w = (const uint8_t*)w2_p;
     dn.ws = (const uint8_t*)s2_p;
-    dn.xcd_run = P.H >= 256 ? 4 * (P.H / 256) : 1;
-    if (const char* env = getenv("MXMOE_XCD_RUN_DN")) dn.xcd_run = atoi(env);  // A/B knob
+    dn.xcd_run = unit_run(P.H >= 256 ? 4 * (P.H / 256) : 1, tn.xcd_run_dn);
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
     if (P.fuse_final) {

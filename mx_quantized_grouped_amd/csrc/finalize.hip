@@ -1,8 +1,6 @@
 // Final rounding of the combined output to bf16. With per-slot rows (fp32 or bf16) the k+1 slot
 // contributions of a token are summed here in fp32 in slot order (a fixed order, so the result is
 // reproducible); with the atomic combine the token-major fp32 accumulator is only converted.
-#include <cstdlib>
-
 #include "device.h"
 #include "kernels.h"
 
@@ -87,8 +85,7 @@ hipError_t launch_finalize(const void* out, int T, int H, int k1, int combine, u
   dim3 grid((unsigned)((n + 255) / 256)), block(256);
   // bf16 slot rows are read once: non-temporal loads keep them from displacing cached data.
   // Measured at 8K tokens (hidden 3072, 9 slots): 105 -> 84 us (non-temporal y stores as well: 89).
-  const char* env = getenv("MXMOE_NT");  // A/B knob: 0 plain loads
-  const bool nt = env ? atoi(env) != 0 : true;
+  const bool nt = tuning().final_nt != 0;  // unset (-1): non-temporal
   if (combine == 1) hipLaunchKernelGGL((k_finalize<1, false>), grid, block, 0, st, out, T, H, k1, y);
   else if (combine == 3 && nt) hipLaunchKernelGGL((k_finalize<3, true>), grid, block, 0, st, out, T, H, k1, y);
   else if (combine == 3) hipLaunchKernelGGL((k_finalize<3, false>), grid, block, 0, st, out, T, H, k1, y);

@@ -245,13 +245,22 @@ hipError_t launch_gate_f(const uint16_t* x, const uint16_t* wg, int T, int H, in
 
 }  // namespace
 
+bool valid_gate_tile(int tile) {
+  switch (tile) {
+    case 11: case 12: case 14: case 21: case 22: case 24: case 28: case 41: case 42: case 44:
+    case 48: case 84: case 124: case 142: case 144: case 148: return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_gate(const uint16_t* x, const uint16_t* wg, int T, int H, int E, bool f32,
-                       void* out, hipStream_t st) {
+                       void* out, int tile, hipStream_t st) {
+  // tile: 10 * TM + F for register tiles, 100 + 10 * TM + F for LDS-staged ones; 0 = by shape
   int cfg = T <= 256 ? 11
             : E >= 512 ? (T <= 1024 ? 124 : 144)
                        : (T <= 1024 ? 12 : (T <= 4096 ? 124 : 142));
-  // A/B knob: 10 * TM + F for register tiles, 100 + 10 * TM + F for LDS-staged ones
-  if (const char* env = getenv("MXMOE_GATE_TILE")) cfg = atoi(env);
+  if (tile) cfg = tile;
+  else if (valid_gate_tile(tuning().gate_tile)) cfg = tuning().gate_tile;
   switch (cfg) {
     case 11: return launch_gate_f<1, 1>(x, wg, T, H, E, f32, out, st);
     case 12: return launch_gate_f<1, 2>(x, wg, T, H, E, f32, out, st);

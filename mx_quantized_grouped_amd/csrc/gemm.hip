@@ -22,7 +22,6 @@
 // more than one tile reads its weights from HBM once, the grouped-MoE program ordering of the
 // MiniMax-M3 page's local-shapes passage.
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -794,10 +793,8 @@ constexpr int kSplitKMaxUnits = 1024;
 // against 2; 1 stage 121 us); for fp8 1 to 3 stages give the same time.
 inline int stream_depth(int wf, int nks) {
   int dmax = wf == WF_BF16 ? 2 : (wf == WF_FP8 ? 3 : 2);
-  if (const char* env = getenv("MXMOE_STREAM_DEPTH")) {  // A/B knob: 1..4
-    int d = atoi(env);
-    if (d >= 1 && d <= 4) dmax = wf == WF_BF16 ? (d < 2 ? d : 2) : d;
-  }
+  const int d = tuning().stream_depth;
+  if (d >= 1 && d <= 4) dmax = wf == WF_BF16 ? (d < 2 ? d : 2) : d;
   for (int d = dmax; d > 1; --d)
     if (nks % d == 0) return d;
   return 1;
@@ -810,12 +807,12 @@ inline int stream_depth(int wf, int nks) {
 // does its memory work meanwhile): 8K-token gate_up 204.7 -> 198.3 us; the fp4 down pass went
 // 87.2 -> 89.2 us at 4096 tokens x 512 experts, so gate_up only.
 inline bool tile_prio(bool gate_up) {
-  if (const char* env = getenv("MXMOE_PRIO")) return atoi(env) != 0;  // A/B knob
+  if (tuning().prio >= 0) return tuning().prio != 0;
   return gate_up;
 }
 
 inline bool tile_pipe(bool gate_up, int wf) {
-  if (const char* env = getenv("MXMOE_TILE_PIPE")) return atoi(env) != 0;  // A/B knob
+  if (tuning().tile_pipe >= 0) return tuning().tile_pipe != 0;
   return gate_up || wf == WF_FP4;
 }
 

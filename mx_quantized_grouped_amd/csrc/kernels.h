@@ -10,11 +10,33 @@ constexpr int kMaxTopK = 63;      // one wave holds the selected experts, lane t
 constexpr int kMaxExperts = 1024; // routed experts; E + 1 <= 2048 for the block-wide scans
 constexpr int kAlignSmallMaxSlots = 4096;
 constexpr int kAlignChunk = 1024; // slots per workgroup in the multi-workgroup sort
+// Buffers addressed through 32-bit offsets (buffer descriptors, row offsets) stay below 2 GiB; the
+// out-of-range sentinel 0x80000000 must never be a valid offset.
+constexpr size_t kMaxBufferBytes = (size_t)1 << 31;
+
+// A/B switches of the measurements behind the kernels' defaults, read from the environment once
+// (at the library's first call); -1 = unset, the library's own choice. They never change a result
+// beyond the documented variants (unit orders, cache hints, pipelining, tile shapes).
+struct Tuning {
+  bool trace;          // MXMOE_TRACE: print the plan of every forward call
+  int w_nt;            // MXMOE_W_NT: non-temporal weight loads of the small-M launcher (0/1)
+  int xcd_order;       // MXMOE_XCD_ORDER: small-M unit order, 1 per-XCD ranges, 0 linear
+  int xcd_run_gu;      // MXMOE_XCD_RUN_GU / _DN: large-M run of units per XCD turn
+  int xcd_run_dn;      //   (0 one range per XCD, 1 linear); -1 unset
+  int stream_depth;    // MXMOE_STREAM_DEPTH: small-M register ring depth 1..4
+  int prio;            // MXMOE_PRIO: raised wave priority during the large-M MFMAs (0/1)
+  int tile_pipe;       // MXMOE_TILE_PIPE: pipelined large-M K-steps (0/1)
+  int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
+  int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
+};
+const Tuning& tuning();
 
 // route.hip
 // gate.hip
+// tile: 0 = chosen by shape; otherwise one of the tiles valid_gate_tile accepts
+bool valid_gate_tile(int tile);
 hipError_t launch_gate(const uint16_t* x, const uint16_t* w_gate, int T, int H, int E, bool out_f32,
-                       void* logits, hipStream_t st);
+                       void* logits, int tile, hipStream_t st);
 
 hipError_t launch_route(const void* logits, bool logits_f32, int T, int E, int top_k,
                         int32_t* ids, float* w, hipStream_t st);

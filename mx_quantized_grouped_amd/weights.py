@@ -42,6 +42,24 @@ class ExpertLoader:
             B.mxmoe_quantize(t2.float().contiguous(), f, codes=self.w2[e], scales=self.s2[e])
         self._seen[e] = True
 
+    def add_expert_mx(self, e: int, c13, s13, c2, s2):
+        """Canonical MX codes and scale bytes of expert e as they are: c13 [2I, H] and c2 [H, I]
+        one code per byte (E2M1 codes are packed here, element 2i in the low nibble), s13
+        [2I, H/32] and s2 [H, I/32] scale bytes."""
+        if self.fmt == B.MXMOE_BF16:
+            raise ValueError("bf16 weights carry no MX codes")
+
+        def codes(c):
+            c = np.asarray(c, dtype=np.uint8)
+            if self.fmt == B.MXMOE_MXFP4_E2M1:
+                c = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+            return torch.from_numpy(np.ascontiguousarray(c)).to(self.device)
+        self.w13[e].copy_(codes(c13))
+        self.w2[e].copy_(codes(c2))
+        self.s13[e].copy_(torch.from_numpy(np.ascontiguousarray(s13, dtype=np.uint8)).to(self.device))
+        self.s2[e].copy_(torch.from_numpy(np.ascontiguousarray(s2, dtype=np.uint8)).to(self.device))
+        self._seen[e] = True
+
     def finish(self, keep_canonical: bool = False):
         """Prepack; returns the packed tuple (w13_p, s13_p, w2_p, s2_p)."""
         if not self._seen.all():

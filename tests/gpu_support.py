@@ -52,6 +52,31 @@ def oracle_weights(w: workloads.Workload) -> moe.ExpertWeights:
                                         w.w_fmt)
 
 
+def oracle_weights_prefetched(w: workloads.Workload, experts, threads: int = 8,
+                              ahead: int = 24) -> moe.ExpertWeights:
+    """The oracle's expert weights for the experts a block computation will ask for, in the order
+    it asks (ascending id), decoded ahead of use on a thread pool: the same per-expert decode, only
+    overlapped (each expert takes ~0.5 s of numpy work at these sizes). At most `ahead` decoded
+    experts are held at once."""
+    from concurrent.futures import ThreadPoolExecutor
+    decode = oracle_weights(w)._get
+    order = [int(e) for e in sorted(set(int(e) for e in experts))]
+    pool = ThreadPoolExecutor(threads)
+    futs, nxt = {}, [0]
+
+    def get(e):
+        i = order.index(e) if e in order else -1
+        while nxt[0] < len(order) and nxt[0] <= i + ahead:
+            futs[order[nxt[0]]] = pool.submit(decode, order[nxt[0]])
+            nxt[0] += 1
+        f = futs.pop(e, None)
+        out = f.result() if f is not None else decode(e)
+        if nxt[0] >= len(order) and not futs:
+            pool.shutdown(wait=False)
+        return out
+    return moe.ExpertWeights(w.E, w.H, w.I, w.w_fmt, get, cache=0)
+
+
 @functools.lru_cache(maxsize=16)
 def inputs(name: str):
     w = workloads.get(name)
@@ -67,12 +92,39 @@ def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
     return np.unique(np.concatenate([[0, T - 1], mid]))
 
 
+# Workloads up to this many tokens are compared on every token; larger ones on a sample that
+# puts at least one compared slot in every tile of the layout the large-M launcher uses.
+FULL_COMPARE_MAX_T = 128
+
+
+def covering_tokens(name: str, block_m: int = 128, seed: int = 0) -> np.ndarray:
+    """Tokens of a workload such that every block_m-row tile of its sorted layout (the oracle's
+    route and align) holds at least one slot of a chosen token, plus the first and last token.
+    Within a tile the slot is drawn at random, so different rows of the tiles are covered."""
+    w, _, lb = inputs(name)
+    if w.T <= FULL_COMPARE_MAX_T:
+        return np.arange(w.T)
+    ids, _ = moe.route(f64(lb), w.top_k)
+    L = moe.align(ids, w.E, block_m)
+    S = w.slots
+    rng = np.random.default_rng(seed)
+    toks = {0, w.T - 1}
+    for b in range(L.num_post_pad // block_m):
+        rows = L.sorted_ids[b * block_m:(b + 1) * block_m]
+        valid = rows[rows < S]
+        if not any(int(f) // (w.top_k + 1) in toks for f in valid):
+            toks.add(int(rng.choice(valid)) // (w.top_k + 1))
+    return np.array(sorted(toks))
+
+
 @functools.lru_cache(maxsize=16)
-def oracle_result(name: str, n_sample: int):
+def oracle_result(name: str):
+    """The oracle on every token (T <= 128) or on the tile-covering sample."""
     w, xb, lb = inputs(name)
-    toks = sample_tokens(w.T, n_sample)
-    r = moe.moe_block(f64(xb), f64(lb), oracle_weights(w), w.top_k, w.act_fmt, tokens=toks)
-    return r
+    toks = covering_tokens(name)
+    ids, _ = moe.route(f64(lb)[toks], w.top_k)
+    W = oracle_weights_prefetched(w, np.unique(ids))
+    return moe.moe_block(f64(xb), f64(lb), W, w.top_k, w.act_fmt, tokens=toks)
 
 
 def tolerance_ok(stats: dict) -> bool:

@@ -156,5 +156,44 @@ def test_workspace_view(L):
     assert nb == 32 * 96                                 # 3072 / 32 scale bytes, already 16-aligned
     sb = B.Shape.of(16, 256, 8, 2, 128, "bf16")
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_XQ)[1] == 0   # bf16 weights: no activation codes
+    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_H)
+    cap = L.mxmoe_align_capacity(32, 128, 8, 16)
+    assert nb == cap * 384 and off % 256 == 0            # I = 384 is three whole 128-K steps
+    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_HS)
+    assert nb == cap * 16                                # 12 scale bytes padded to 16
+    assert B.mxmoe_workspace_view(sb, None, B.VIEW_H)[1] == L.mxmoe_align_capacity(16, 8, 2, 16) * 128 * 2
+    assert B.mxmoe_workspace_view(sb, None, B.VIEW_HS)[1] == 0
     with pytest.raises(B.MxMoeError):
-        B.mxmoe_workspace_view(s, None, 9)
+        B.mxmoe_workspace_view(s, None, 10)
+    with pytest.raises(B.MxMoeError):
+        B.mxmoe_workspace_view(s, None, -1)
+
+
+def test_options_unit_run(L):
+    s = B.Shape.of(8192, 3072, 128, 8, 384, "mxfp8")
+    assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, -1)) > 0     # one range per XCD
+    assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, 5)) > 0      # runs of 5
+    assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, -2)) == 0    # invalid
+
+
+def test_gate_ex_tiles(L):
+    p = ctypes.c_void_p(4096)
+    assert L.mxmoe_gate_ex(p, p, 4, 128, 8, 1, 13, p, None) == B.MXMOE_EINVAL   # no such tile
+    assert L.mxmoe_gate_ex(p, p, 4, 128, 8, 1, 99, p, None) == B.MXMOE_EINVAL
+    assert L.mxmoe_gate_ex(None, None, 0, 128, 8, 1, 144, None, None) == B.MXMOE_OK  # T = 0
+
+
+def test_32bit_offset_limits(L):
+    # Activation codes, the intermediate and one expert's weights are addressed with 32-bit
+    # offsets: shapes that would reach 2 GiB are refused on the host, before any HIP call.
+    big = B.Shape.of(700000, 3072, 128, 8, 384, "mxfp8")       # T*H = 2.15 GB of codes
+    assert B.mxmoe_workspace_bytes(big) == 0
+    assert L.mxmoe_forward(ctypes.byref(big), *[ctypes.c_void_p(4096)] * 7,
+                           ctypes.c_void_p(4096), 1 << 40, None) == B.MXMOE_EUNSUPPORTED
+    # bf16 weights, I = 4096: the intermediate (cap * I * 2 bytes) crosses 2 GiB near 29K tokens
+    assert B.mxmoe_workspace_bytes(B.Shape.of(20000, 1024, 8, 2, 4096, "bf16")) > 0
+    assert B.mxmoe_workspace_bytes(B.Shape.of(90000, 1024, 8, 2, 4096, "bf16")) == 0
+    # one expert's W13 past 2 GiB (2 * I * H bytes of E4M3 codes)
+    huge_w = B.Shape.of(4, 32768, 4, 2, 32768, "mxfp8")
+    assert B.mxmoe_prepacked_bytes(huge_w, 0) == 0 and B.mxmoe_workspace_bytes(huge_w) == 0
+    assert B.mxmoe_prepacked_bytes(B.Shape.of(4, 16384, 4, 2, 32768, "mxfp4"), 0) > 0

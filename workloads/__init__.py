@@ -165,3 +165,58 @@ def draw_all_experts(w: Workload, threads: int = 8, callback=None):
             else:
                 callback(e, a, b)
     return out
+
+
+# ---------------------------------------------------------------- exact-arithmetic draws
+def draw_exact_block(T: int, H: int, E: int, top_k: int, I: int, seed: int = 0):
+    """Inputs on which every step of the block is exact in fp32, for bit-for-bit parity checks of
+    the GEMM operand and scale layouts (the integer-exact construction).
+
+    Every value is a small integer times a power of two, chosen so that its MX block maximum makes
+    it land on the E4M3 and E2M1 grids exactly (no rounding at Q1 or at weight quantisation):
+      * x[t, h]: one of 0, +-1, +-2 times 2^p (p in -1..1, per 32-block), except x[t, 0] = 16 (its
+        block keeps p = 0). bf16-exact.
+      * logits: for each token top_k distinct experts get 1.0, the others one of -1, -0.5, 0, 0.5;
+        the selected logits are equal, so every routed weight is exp(0) / top_k (top_k a power of
+        two keeps it exact) and ties order the selection by expert index.
+      * W13 gate row n < I: 4 at column 0, and 4 further columns with +-2^p (p in -1..0 per
+        block); with x[t, 0] = 16 the gate pre-activation is then 64 +- 16 >= 48, where
+        SiLU(g) = g / (1 + e^-g) equals g in fp32 and fp64 (e^-48 < 2^-53).
+      * W13 up row: 16 columns with one of +-1, +-2 times 2^p (p in -1..1 per block); in every
+        32-block holding a nonzero, the largest magnitude is 1 or 2 times 2^p.
+      * W2 row: about one column in eight with one of +-1, +-2 times 2^p.
+    Returns (x bf16 bits [T, H], logits bf16 bits [T, E], [(w13 fp32 [2I, H], w2 fp32 [H, I])]
+    for experts 0..E)."""
+    if top_k & (top_k - 1):
+        raise ValueError("top_k must be a power of two for exact routing weights")
+    rng = _rng(seed, 9)
+    nb = H // 32
+
+    def block_pow(rows, blocks, lo, hi):
+        return np.repeat(2.0 ** rng.integers(lo, hi + 1, size=(rows, blocks)), 32, axis=1)
+
+    x = rng.integers(-2, 3, size=(T, H)).astype(np.float64) * block_pow(T, nb, -1, 1)
+    x[:, :32] = rng.integers(-2, 3, size=(T, 32))
+    x[:, 0] = 16.0
+    lg = rng.choice(np.array([-1.0, -0.5, 0.0, 0.5]), size=(T, E))
+    for t in range(T):
+        lg[t, rng.choice(E, size=top_k, replace=False)] = 1.0
+    experts = []
+    for _ in range(E + 1):
+        w13 = np.zeros((2 * I, H))
+        gp = block_pow(I, nb, -1, 0)
+        for n in range(I):
+            w13[n, 0] = 4.0
+            cols = rng.choice(np.arange(1, H), size=4, replace=False)
+            w13[n, cols] = rng.choice([-1.0, 1.0], size=4) * gp[n, cols]
+        up = block_pow(I, nb, -1, 1)
+        for n in range(I):
+            cols = rng.choice(H, size=16, replace=False)
+            w13[I + n, cols] = rng.choice([-2.0, -1.0, 1.0, 2.0], size=16) * up[n, cols]
+        w2 = np.zeros((H, I))
+        dp = block_pow(H, I // 32, -1, 1)
+        mask = rng.random((H, I)) < 0.125
+        w2[mask] = rng.choice([-2.0, -1.0, 1.0, 2.0], size=int(mask.sum())) * dp[mask]
+        experts.append((w13.astype(np.float32), w2.astype(np.float32)))
+    return (bf16_bits_from_f32(x.astype(np.float32)), bf16_bits_from_f32(lg.astype(np.float32)),
+            experts)
