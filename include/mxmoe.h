@@ -189,6 +189,22 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
                      const void* s2_p, void* y, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ------------------------------------------------------------------------ forward, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): mxmoe_forward with the automatic plan, its workspace
+ * being a device-resident array inside the library of MXMOE_NOALLOC_SCRATCH_BYTES per GPU (each
+ * GPU the library runs on holds it until the process ends). The caller passes inputs, weights
+ * and the output as for mxmoe_forward; the stream must belong to the current device. The call
+ * allocates and frees nothing. A shape whose workspace (mxmoe_workspace_bytes) exceeds the array
+ * returns MXMOE_EWORKSPACE before any HIP call. Every call on one GPU uses the same array and
+ * leaves its contents behind; forward needs no initialised workspace, so nothing is cleared, but
+ * calls that overlap on one GPU (other streams, other host threads) race on the array and must
+ * be serialised by the caller. */
+#define MXMOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mxmoe_forward_noalloc(const mxmoe_shape* s, const void* x, const void* logits,
+                          const void* w13_p, const void* s13_p, const void* w2_p, const void* s2_p,
+                          void* y, void* stream);
+
 /* Host: where forward keeps an intermediate inside its workspace, for inspection after the call
  * (routing table, sorted layout, quantised activations, quantised SwiGLU output). which:
  * 0 topk_ids, 1 topk_w, 2 sorted_ids, 3 block_expert, 4 num_post_pad, 5 expert_off,

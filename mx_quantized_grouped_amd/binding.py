@@ -28,7 +28,7 @@ EXPORTS = [
     "mxmoe_status_string", "mxmoe_gate", "mxmoe_gate_ex", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
     "mxmoe_align", "mxmoe_quantize", "mxmoe_prepacked_bytes", "mxmoe_prepack",
     "mxmoe_workspace_bytes", "mxmoe_workspace_bytes_ex", "mxmoe_forward", "mxmoe_forward_ex",
-    "mxmoe_workspace_view",
+    "mxmoe_workspace_view", "mxmoe_forward_noalloc",
 ]
 
 
@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
         "mxmoe_forward": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mxmoe_forward_ex": (i32, [sp, op, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mxmoe_workspace_view": (sz, [sp, op, i32, ctypes.POINTER(sz), ctypes.POINTER(i32)]),
+        "mxmoe_forward_noalloc": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -249,4 +250,18 @@ def mxmoe_forward(shape: Shape, x, logits, packed, y=None, workspace=None,
     else:
         st = lib().mxmoe_forward_ex(ctypes.byref(shape), ctypes.byref(options), *args)
     _check(st, "mxmoe_forward")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def mxmoe_forward_noalloc(shape: Shape, x, logits, packed, y=None, stream=None):
+    """mxmoe_forward with the library's device-resident workspace (no workspace argument)."""
+    if y is None:
+        y = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=_dev(x))
+    w13p, s13p, w2p, s2p = packed
+    _check(lib().mxmoe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(logits), _ptr(w13p),
+                                       _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(y), _stream(stream)),
+           "mxmoe_forward_noalloc")
     return y
