@@ -93,7 +93,7 @@ class GpuWorkload:
         self.xb, self.lb = workloads.draw_x(w), workloads.draw_logits(w)
         self.x, self.logits = to_dev(self.xb), to_dev(self.lb)
         self.y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
-        self.ws = torch.empty(B.mxmoe_workspace_bytes(self.shape), dtype=torch.uint8, device="cuda")
+        self.ws = B.new_workspace(B.mxmoe_workspace_bytes(self.shape), "cuda")
 
     def step(self, i, options=None):
         self.B.mxmoe_forward(self.shape, self.x, self.logits, self.packed[i % len(self.packed)],

@@ -91,6 +91,18 @@ typedef struct {
      activation quantisation), before gate_up, before down, before the final bf16 rounding, and
      after it. NULL = no events. */
   void** stage_events;
+  /* The whole block in one launch for small batches (routing, layout, gate_up, down and the final
+     sum as roles of one grid; small-M plan with 16-row tiles and fp32 slot rows): 0 = the
+     library's choice, 1 = required (MXMOE_EUNSUPPORTED if the shape or the other options do not
+     allow it), -1 = never. */
+  int32_t fused;
+  /* One-launch path: polls of a bounded wait before it gives up (0 = the default, about 50 ms).
+     A wait that gives up skips the work that depended on it, every workgroup still ends, and the
+     status word (workspace view MXMOE_VIEW_STATUS) reads 1 after the call. */
+  int32_t spin_limit;
+  int32_t hold;     /* tests only: 1 = the one-launch path never publishes its layout, so every
+                       wait on it gives up (exercises the bounded waits); 0 otherwise */
+  int32_t reserved; /* must be 0 */
 } mxmoe_options;
 #define MXMOE_STAGE_EVENTS 5
 
@@ -177,8 +189,12 @@ int mxmoe_prepack(const mxmoe_shape* s, const void* w13, const uint8_t* s13, con
 /* ------------------------------------------------------------------------------- forward
  * The whole block. x [T, H] bf16; logits [T, E] (logits_dtype); prepacked weights from
  * mxmoe_prepack; y [T, H] bf16, overwritten. workspace: device scratch of at least
- * mxmoe_workspace_bytes(s) (or _ex with the same options), 256-byte aligned; its contents need
- * no initialisation and are clobbered. */
+ * mxmoe_workspace_bytes(s) (or _ex with the same options), 256-byte aligned. Its first
+ * MXMOE_WORKSPACE_CONTROL_BYTES bytes are the control words of the one-launch path: they must be
+ * zero before the workspace's first forward call (allocate it zeroed or clear it once), and every
+ * call leaves them zero again, also a call whose waits gave up. The rest of the workspace needs no
+ * initialisation and is clobbered. */
+#define MXMOE_WORKSPACE_CONTROL_BYTES (72u * 1024u)
 size_t mxmoe_workspace_bytes(const mxmoe_shape* s);
 size_t mxmoe_workspace_bytes_ex(const mxmoe_shape* s, const mxmoe_options* opt);
 int mxmoe_forward(const mxmoe_shape* s, const void* x, const void* logits, const void* w13_p,
@@ -214,9 +230,12 @@ int mxmoe_forward_noalloc(const mxmoe_shape* s, const void* x, const void* logit
  * slot sorted_ids[r]; Ip = I rounded up to a multiple of 128; E4M3 codes for MX weights, bf16
  * values for bf16 weights), 9 intermediate scale bytes [cap, srs_I] (K-block order, srs_I = Ip/32
  * rounded up to a multiple of 16; MX weights only). Rows of padding slots and columns past I are
- * unspecified. Returns the byte offset and writes the byte size to *bytes; the tile height forward
- * used is written to *block_m. Returns (size_t)-1 for an invalid request. */
-#define MXMOE_VIEW_COUNT 10
+ * unspecified. 10 (MXMOE_VIEW_STATUS) the status word of the last one-launch call on this
+ * workspace (int32: 0 every wait completed, 1 a bounded wait gave up and the output is not valid).
+ * Returns the byte offset and writes the byte size to *bytes; the tile height forward used is
+ * written to *block_m. Returns (size_t)-1 for an invalid request. */
+#define MXMOE_VIEW_STATUS 10
+#define MXMOE_VIEW_COUNT 11
 size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int which,
                             size_t* bytes, int* block_m);
 

@@ -19,7 +19,8 @@ MXMOE_BF16, MXMOE_F32, MXMOE_MXFP8_E4M3, MXMOE_MXFP4_E2M1 = 0, 1, 2, 3
 MXMOE_LAUNCH_AUTO, MXMOE_LAUNCH_SMALL_M, MXMOE_LAUNCH_LARGE_M = 0, 1, 2
 MXMOE_COMBINE_AUTO, MXMOE_COMBINE_SLOTS, MXMOE_COMBINE_ATOMIC, MXMOE_COMBINE_SLOTS_BF16 = 0, 1, 2, 3
 (VIEW_TOPK_IDS, VIEW_TOPK_W, VIEW_SORTED_IDS, VIEW_BLOCK_EXPERT, VIEW_NUM_POST_PAD, VIEW_EXPERT_OFF,
- VIEW_XQ, VIEW_XS, VIEW_H, VIEW_HS) = range(10)
+ VIEW_XQ, VIEW_XS, VIEW_H, VIEW_HS, VIEW_STATUS) = range(11)
+WORKSPACE_CONTROL_BYTES = 72 * 1024
 
 FMT_BY_NAME = {"bf16": MXMOE_BF16, "f32": MXMOE_F32, "mxfp8": MXMOE_MXFP8_E4M3,
                "mxfp4": MXMOE_MXFP4_E2M1}
@@ -56,7 +57,9 @@ STAGES = ("prologue", "gate_up", "down", "finalize")
 class Options(ctypes.Structure):
     _fields_ = [("launcher", ctypes.c_int32), ("combine", ctypes.c_int32),
                 ("block_m", ctypes.c_int32), ("unit_run", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("fused", ctypes.c_int32), ("spin_limit", ctypes.c_int32),
+                ("hold", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MxMoeError(RuntimeError):
@@ -234,14 +237,26 @@ def mxmoe_workspace_view(shape: Shape, options: Options | None, which: int):
     return int(off), int(nb.value), int(bm.value)
 
 
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A forward workspace of nbytes, zero-filled (its control words must start at zero; every
+    forward call leaves them zero, so it can be reused for any later call)."""
+    return torch.zeros(max(int(nbytes), WORKSPACE_CONTROL_BYTES), dtype=torch.uint8, device=device)
+
+
+def workspace_status(shape: Shape, workspace: torch.Tensor, options: Options | None = None) -> int:
+    """Status word of the last one-launch forward on this workspace (0 ok, 1 a wait gave up)."""
+    off, nb, _ = mxmoe_workspace_view(shape, options, VIEW_STATUS)
+    return int(workspace[off:off + nb].view(torch.int32).item())
+
+
 def mxmoe_forward(shape: Shape, x, logits, packed, y=None, workspace=None,
                   options: Options | None = None, stream=None):
     """packed = (w13_p, s13_p, w2_p, s2_p) from mxmoe_prepack (scales may be None for bf16)."""
     if y is None:
         y = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=_dev(x))
     need = mxmoe_workspace_bytes(shape, options)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=_dev(x))
+    if workspace is None:  # zeroed: the control words must start at zero
+        workspace = new_workspace(need, _dev(x))
     w13p, s13p, w2p, s2p = packed
     args = [_ptr(x), _ptr(logits), _ptr(w13p), _ptr(s13p), _ptr(w2p), _ptr(s2p), _ptr(y),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)]

@@ -93,7 +93,7 @@ int check_shape(const mxmoe_shape* s) {
 }
 
 enum Seg {
-  SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF, SEG_TOUCHED, SEG_ALIGN,
+  SEG_CTL, SEG_IDS, SEG_W, SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS, SEG_EXPOFF, SEG_TOUCHED, SEG_ALIGN,
   SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_OUT, SEG_DONE, SEG_SORTW, NSEG
 };
 
@@ -105,6 +105,8 @@ struct Plan {
   bool fuse_final;  // final bf16 rounding inside the down pass (small M, atomic combine)
   int bm, cap, Ip, srs_H, srs_I;
   int unit_run;  // large-M unit order from the options (0 = the launcher's default)
+  bool fused;    // the one-launch path (small batches)
+  int spin_limit, hold;
   size_t off[NSEG + 1];
 };
 
@@ -123,8 +125,9 @@ bool within_offsets(const mxmoe_shape* s, int T, int cap, int Ip, int srs_H, int
 int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   int rc = check_shape(s);
   if (rc) return rc;
-  mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr};
-  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.unit_run < -1)
+  mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr, 0, 0, 0, 0};
+  if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.unit_run < -1 ||
+      o.fused < -1 || o.fused > 1 || o.spin_limit < 0 || o.hold < 0 || o.hold > 1 || o.reserved)
     return MXMOE_EINVAL;
   if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
   Plan& p = *P;
@@ -135,6 +138,17 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   // Launcher: block-major (large-M) once the average expert holds enough rows to fill tiles.
   p.large = o.launcher == MXMOE_LAUNCH_LARGE_M ||
             (o.launcher == MXMOE_LAUNCH_AUTO && p.S >= 16 * p.E1);
+  // One launch for the whole block: small batches with the small-M plan (16-row tiles, fp32 slot
+  // rows) whose layout fits the layout workgroup.
+  const bool fused_ok = o.launcher != MXMOE_LAUNCH_LARGE_M &&
+                        fused_fits(p.wf, p.T, p.H, p.E, p.k, p.I) &&
+                        (o.combine == MXMOE_COMBINE_AUTO || o.combine == MXMOE_COMBINE_SLOTS) &&
+                        (o.block_m == 0 || o.block_m == 16);
+  if (o.fused == 1 && !fused_ok) return MXMOE_EUNSUPPORTED;
+  p.fused = o.fused == 1 && fused_ok;
+  if (p.fused) p.large = false;  // the one-launch path is a small-M plan
+  p.spin_limit = o.spin_limit ? o.spin_limit : kFusedDefaultSpin;
+  p.hold = o.hold;
   // Large batches write bf16 slot rows (fp32 atomics run at about one value per L2 channel per
   // cycle, far below what the prefill combine needs); small batches write fp32 slot rows. The
   // atomic combine at small M rounds to bf16 inside the down pass (no final launch), but waiting
@@ -150,6 +164,7 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.unit_run = o.unit_run;
   if (!within_offsets(s, p.T, p.cap, p.Ip, p.srs_H, p.srs_I, p.mx)) return MXMOE_EUNSUPPORTED;
   size_t sz[NSEG];
+  sz[SEG_CTL] = kFusedCtlBytes;  // first in every plan, so any call may follow any other
   sz[SEG_IDS] = (size_t)p.S * 4;
   sz[SEG_W] = (size_t)p.S * 4;
   sz[SEG_SORTED] = (size_t)p.cap * 4;
@@ -311,15 +326,15 @@ size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int 
   Plan p;
   if (make_plan(s, opt, &p)) return (size_t)-1;
   static const int segs[MXMOE_VIEW_COUNT] = {SEG_IDS, SEG_W,  SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS,
-                                             SEG_EXPOFF, SEG_XQ, SEG_XS, SEG_H, SEG_HS};
+                                             SEG_EXPOFF, SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_CTL};
   if (which < 0 || which >= MXMOE_VIEW_COUNT) return (size_t)-1;
   const size_t sz[MXMOE_VIEW_COUNT] = {
       (size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4, (size_t)(p.cap / p.bm) * 4, 4,
       (size_t)(p.E1 + 1) * 4, p.mx ? (size_t)p.T * p.H : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
-      (size_t)p.cap * p.Ip * (p.mx ? 1 : 2), p.mx ? (size_t)p.cap * p.srs_I : 0};
+      (size_t)p.cap * p.Ip * (p.mx ? 1 : 2), p.mx ? (size_t)p.cap * p.srs_I : 0, 4};
   if (bytes) *bytes = sz[which];
   if (block_m) *block_m = p.bm;
-  return p.off[segs[which]];
+  return p.off[segs[which]] + (which == MXMOE_VIEW_STATUS ? kFusedStatusByte : 0);
 }
 
 int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void* x,
@@ -359,7 +374,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   const Tuning& tn = tuning();
   if (tn.trace)
     fprintf(stderr, "mxmoe_forward: T=%d H=%d E=%d k=%d I=%d w=%d launcher=%s block_m=%d combine=%s\n",
-            P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.large ? "large_m" : "small_m", P.bm,
+            P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.fused ? "one_launch" : (P.large ? "large_m" : "small_m"), P.bm,
             P.combine == 1 ? "slots" : (P.combine == 2 ? "atomic" : "slots_bf16"));
 
   void** ev = opt ? opt->stage_events : nullptr;
@@ -367,6 +382,36 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     return ev ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
+  if (P.fused) {
+    FusedArgs fa{};
+    fa.x = (const uint16_t*)x;
+    fa.logits = logits;
+    fa.logits_f32 = s->logits_dtype == MXMOE_F32;
+    fa.w13 = (const uint8_t*)w13_p;
+    fa.s13 = (const uint8_t*)s13_p;
+    fa.w2 = (const uint8_t*)w2_p;
+    fa.s2 = (const uint8_t*)s2_p;
+    fa.y = (uint16_t*)y;
+    fa.T = P.T; fa.H = P.H; fa.E = P.E; fa.top_k = P.k; fa.I = P.I; fa.Ip = P.Ip;
+    fa.ids = ids;
+    fa.tw = tw;
+    fa.lay = AlignOut{sorted, bexp, counters, eoff, touched, counters + 1, tw, sorted_w};
+    fa.cap = P.cap;
+    fa.xq = xq;
+    fa.xs = xs;
+    fa.srs_H = P.srs_H;
+    fa.h = h;
+    fa.hs = hs;
+    fa.h_stride = P.Ip;
+    fa.srs_I = P.srs_I;
+    fa.slots = out32;
+    fa.ctl = (int32_t*)(ws + P.off[SEG_CTL]);
+    fa.spin_limit = P.spin_limit;
+    fa.hold = P.hold;
+    if (e == hipSuccess) e = launch_fused(P.wf, fa, st);
+    for (int i = 1; i < MXMOE_STAGE_EVENTS && e == hipSuccess; ++i) e = mark(i);
+    return hip_status(e);
+  }
   PrologueArgs pa;
   pa.logits = logits;
   pa.T = P.T;

@@ -145,6 +145,42 @@ struct GemmParams {
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 
+// fused.hip: the whole block for small batches in one launch (routing, layout, gate_up, down and
+// the final sum as roles of one grid). Its control words sit at the start of every workspace.
+constexpr size_t kFusedCtlBytes = 72 * 1024;  // zero before the first call; every call resets them
+constexpr int kFusedBitmapWords = 2560;       // per-expert slot bitmaps of the layout workgroup
+constexpr int kFusedMaxFin = 16384;           // final-sum counters: (H / 64) * ceil(T / 8)
+constexpr int kFusedMaxT = 128;
+constexpr int kFusedDefaultSpin = 50000;      // polls (each ~1 us) before a wait gives up
+constexpr size_t kFusedStatusByte = 16;       // offset of the status word in the control words
+struct FusedArgs {
+  const uint16_t* x;      // bf16 [T, H]
+  const void* logits;     // [T, E]
+  bool logits_f32;
+  const uint8_t* w13;     // prepacked weights and scales
+  const uint8_t* s13;
+  const uint8_t* w2;
+  const uint8_t* s2;
+  uint16_t* y;            // bf16 [T, H]
+  int T, H, E, top_k, I, Ip;
+  int32_t* ids;           // [T, k + 1] routing table
+  float* tw;
+  AlignOut lay;           // the 16-row sorted layout (every field set)
+  int cap;
+  uint8_t* xq;            // activation codes [T, H] and scales [T, srs_H], for inspection
+  uint8_t* xs;
+  int srs_H;
+  uint8_t* h;             // intermediate rows [cap, h_stride] and scales [cap, srs_I]
+  uint8_t* hs;
+  int h_stride, srs_I;
+  float* slots;           // fp32 slot rows [S, H]
+  int32_t* ctl;           // control words (kFusedCtlBytes)
+  int spin_limit;         // polls before a wait gives up
+  int hold;               // tests: the layout is never published, so every wait gives up
+};
+bool fused_fits(int wf, int T, int H, int E, int top_k, int I);
+hipError_t launch_fused(int wf, const FusedArgs& a, hipStream_t st);
+
 // finalize.hip
 // combine: 1 fp32 slot rows, 2 fp32 token rows, 3 bf16 slot rows.
 hipError_t launch_finalize(const void* out, int T, int H, int k1, int combine, uint16_t* y,

@@ -7,7 +7,8 @@
 // only a host-side stand-in for the symbol, never a device address, so host code never passes it
 // anywhere: the device address is looked up once per device with hipGetSymbolAddress (with that
 // device current) and kept in `g_scratch`; kernels receive that pointer as their workspace
-// argument, exactly as they receive a caller's workspace in mxmoe_forward.
+// argument, exactly as they receive a caller's workspace in mxmoe_forward. At the same set-up the
+// array's control words are cleared once, as mxmoe_forward requires of a new workspace.
 #include <mutex>
 
 #include "mxmoe.h"
@@ -29,6 +30,8 @@ int scratch_of_current_device(void** out) {
   if (!g_scratch[dev]) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXMOE_EHIP;
+    // the workspace's control words start at zero (every forward call leaves them zero)
+    if (hipMemset(p, 0, MXMOE_WORKSPACE_CONTROL_BYTES) != hipSuccess) return MXMOE_EHIP;
     g_scratch[dev] = p;
   }
   *out = g_scratch[dev];

@@ -146,7 +146,11 @@ def test_forward_workspace_checks(L):
 def test_workspace_view(L):
     s = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
     off0, nb0, bm = B.mxmoe_workspace_view(s, None, B.VIEW_TOPK_IDS)
-    assert off0 == 0 and nb0 == 32 * 9 * 4 and bm == 16   # small-M default tile: 16 rows
+    # the control words of the one-launch path come first, at the same place in every plan
+    assert off0 == B.WORKSPACE_CONTROL_BYTES and nb0 == 32 * 9 * 4 and bm == 16
+    assert B.mxmoe_workspace_view(s, None, B.VIEW_STATUS)[:2] == (16, 4)
+    big = B.Shape.of(8192, 3072, 128, 8, 384, "mxfp8")
+    assert B.mxmoe_workspace_view(big, None, B.VIEW_STATUS)[:2] == (16, 4)
     off, nb, bm = B.mxmoe_workspace_view(s, B.Options(2, 2, 128, 0), B.VIEW_SORTED_IDS)
     assert bm == 128 and nb == 4 * L.mxmoe_align_capacity(32, 128, 8, 128)
     assert off % 256 == 0
@@ -164,9 +168,25 @@ def test_workspace_view(L):
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_H)[1] == L.mxmoe_align_capacity(16, 8, 2, 16) * 128 * 2
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_HS)[1] == 0
     with pytest.raises(B.MxMoeError):
-        B.mxmoe_workspace_view(s, None, 10)
+        B.mxmoe_workspace_view(s, None, 11)
     with pytest.raises(B.MxMoeError):
         B.mxmoe_workspace_view(s, None, -1)
+
+
+def test_options_one_launch(L):
+    dec = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
+    fused = B.Options(0, 0, 0, 0, None, 1)
+    assert B.mxmoe_workspace_bytes(dec, fused) > 0
+    # required but not allowed: large batches, bf16 weights, other combines or tile heights
+    assert B.mxmoe_workspace_bytes(B.Shape.of(8192, 3072, 128, 8, 384, "mxfp8"), fused) == 0
+    assert B.mxmoe_workspace_bytes(B.Shape.of(16, 256, 8, 2, 128, "bf16"), fused) == 0
+    assert B.mxmoe_workspace_bytes(dec, B.Options(0, 3, 0, 0, None, 1)) == 0
+    assert B.mxmoe_workspace_bytes(dec, B.Options(0, 0, 64, 0, None, 1)) == 0
+    assert B.mxmoe_workspace_bytes(dec, B.Options(2, 0, 0, 0, None, 1)) == 0
+    # invalid values
+    for o in [B.Options(0, 0, 0, 0, None, 2), B.Options(0, 0, 0, 0, None, 0, -1),
+              B.Options(0, 0, 0, 0, None, 0, 0, 2), B.Options(0, 0, 0, 0, None, 0, 0, 0, 1)]:
+        assert B.mxmoe_workspace_bytes(dec, o) == 0
 
 
 def test_options_unit_run(L):

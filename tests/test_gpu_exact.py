@@ -37,7 +37,7 @@ CASES = [  # T, H, E, top_k, I, weight format
     (40, 384, 6, 4, 128, "mxfp8"),
     (20, 256, 8, 2, 128, "bf16"),
 ]
-OPTIONS = [None, (1, 1, 0), (1, 2, 0), (2, 1, 0), (2, 2, 0), (2, 1, 32), (2, 1, 256)]
+OPTIONS = [None, (1, 1, 0), (1, 2, 0), (2, 1, 0), (2, 2, 0), (2, 1, 32), (2, 1, 256), "one_launch"]
 
 
 def _say(*a):
@@ -113,12 +113,21 @@ def _view(ws, shape, opt, which, dtype):
     return ws[off:off + nb].view(dtype).cpu().numpy(), bm
 
 
-@pytest.mark.parametrize("opt", OPTIONS, ids=lambda o: "auto" if o is None else "l%d_c%d_bm%d" % o)
+def _ids(o):
+    return "auto" if o is None else (o if isinstance(o, str) else "l%d_c%d_bm%d" % o)
+
+
+@pytest.mark.parametrize("opt", OPTIONS, ids=_ids)
 def test_exact_output_and_intermediate(case, opt):
     c = case
-    o = None if opt is None else B.Options(opt[0], opt[1], opt[2], 0)
+    if opt == "one_launch":
+        if c["fmt"] == "bf16" or c["T"] > 128:
+            pytest.skip("the one-launch path takes MX weights and up to 128 tokens")
+        o = B.Options(0, 0, 0, 0, None, 1)
+    else:
+        o = None if opt is None else B.Options(opt[0], opt[1], opt[2], 0)
     _say("forward", c["shape"].T, c["shape"].H, c["fmt"], opt)
-    ws = torch.empty(B.mxmoe_workspace_bytes(c["shape"], o), dtype=torch.uint8, device=DEV)
+    ws = B.new_workspace(B.mxmoe_workspace_bytes(c["shape"], o), DEV)
     y = B.mxmoe_forward(c["shape"], bf16_tensor(c["xb"]), bf16_tensor(c["lb"]), c["packed"],
                         workspace=ws, options=o)
     torch.cuda.synchronize()

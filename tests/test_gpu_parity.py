@@ -172,7 +172,7 @@ def test_gate_then_route_and_forward():
     x = bf16_tensor(xb)
     logits = B.mxmoe_gate(x, bf16_tensor(gb))
     shape = shape_of(w, "f32")
-    ws = torch.empty(B.mxmoe_workspace_bytes(shape, None), dtype=torch.uint8, device=DEV)
+    ws = B.new_workspace(B.mxmoe_workspace_bytes(shape, None), DEV)
     y = B.mxmoe_forward(shape, x, logits, packed, workspace=ws)
     torch.cuda.synchronize()
     lg = logits.cpu().numpy().astype(np.float64)
@@ -273,7 +273,7 @@ def _run_forward(name, options=None, logits_dtype="bf16"):
     shape = shape_of(w, logits_dtype)
     x = bf16_tensor(xb)
     lg = bf16_tensor(lb) if logits_dtype == "bf16" else bf16_tensor(lb).float()
-    ws = torch.empty(B.mxmoe_workspace_bytes(shape, options), dtype=torch.uint8, device=DEV)
+    ws = B.new_workspace(B.mxmoe_workspace_bytes(shape, options), DEV)
     y = B.mxmoe_forward(shape, x, lg, packed, workspace=ws, options=options)
     torch.cuda.synchronize()
     return w, shape, y, ws
@@ -355,7 +355,7 @@ def test_forward_activation_codes_exhaustive_bf16():
         loader.add_expert(e, *workloads.draw_expert(wl, e))
     packed = loader.finish()
     lb = workloads.draw_logits(wl)
-    ws = torch.empty(B.mxmoe_workspace_bytes(shape, None), dtype=torch.uint8, device=DEV)
+    ws = B.new_workspace(B.mxmoe_workspace_bytes(shape, None), DEV)
     B.mxmoe_forward(shape, bf16_tensor(xb), bf16_tensor(lb), packed, workspace=ws)
     torch.cuda.synchronize()
     _check_act_codes(shape, ws, None, xb)
@@ -406,7 +406,7 @@ def test_forward_graph_replay(name):
     draws = [(xb, lb)] + [(xb[rng.permutation(w.T)], lb[rng.permutation(w.T)]) for _ in range(2)]
     xs, ls = bf16_tensor(xb), bf16_tensor(lb)
     ys = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
-    wss = torch.empty(B.mxmoe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    wss = B.new_workspace(B.mxmoe_workspace_bytes(shape), DEV)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
