@@ -30,11 +30,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
-PEAK_MFMA_TFLOPS = {"mxfp8": 5000.0, "mxfp4": 5000.0, "bf16": 2500.0}   # dense; fp8-rate issue
-# for W4A8 (fp8 activations) — the fp4 rate (10.1 PF) needs both operands in 4 bits.
+# Dense MFMA peaks by the operand pair the block issues: bf16 2.5 PFLOP/s; 5.0 when either operand
+# is E4M3 (MXFP8, and MXFP4 weights with MXFP8 activations run at the fp8 rate); 10.1 when both
+# operands are E2M1 (MXFP4 weights with MXFP4 activations).
+PEAK_MFMA_TFLOPS = {("bf16", "bf16"): 2500.0, ("mxfp8", "mxfp8"): 5000.0,
+                    ("mxfp4", "mxfp8"): 5000.0, ("mxfp4", "mxfp4"): 10100.0}
 LLC_BYTES = 256 << 20              # MALL (infinity cache)
 METRIC = "MoE-block TFLOP/s and HBM GB/s (% of MI355X roofline) at decode/prefill M"
 ELEM_BYTES = {"mxfp8": 1.0, "mxfp4": 0.5, "bf16": 2.0}
+
+
+def mfma_peak(w):
+    return PEAK_MFMA_TFLOPS[(w.w_fmt, w.act_fmt)]
 
 
 def log(*a):
@@ -55,9 +62,9 @@ def block_bytes(w, touched):
 
 
 def gate_up_bytes(w, touched):
-    act = 1.0 + (0.0 if w.act_fmt == "bf16" else 1.0 / 32)
-    a_in = w.T * w.H * (2.0 if w.act_fmt == "bf16" else act)
-    h_out = w.slots * w.I * (2.0 if w.act_fmt == "bf16" else act)
+    act = ELEM_BYTES[w.act_fmt] + (0.0 if w.act_fmt == "bf16" else 1.0 / 32)   # codes + scales
+    a_in = w.T * w.H * act
+    h_out = w.slots * w.I * act
     return touched * expert_bytes(w, "w13") + a_in + h_out
 
 
@@ -78,7 +85,7 @@ class GpuWorkload:
         from mx_quantized_grouped_amd.weights import ExpertLoader
         self.torch, self.B = torch, B
         self.w = w = workloads.get(name)
-        self.shape = B.Shape.of(w.T, w.H, w.E, w.top_k, w.I, w.w_fmt)
+        self.shape = B.Shape.of(w.T, w.H, w.E, w.top_k, w.I, w.w_fmt, act_fmt=w.act_fmt)
         t0 = time.time()
         loader = ExpertLoader(self.shape, "cuda")
         workloads.draw_all_experts(w, threads=threads, callback=loader.add_expert)
@@ -221,7 +228,7 @@ def measure(name, steps, warmup):
         "stage_ms": stages,
     }
     res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
-    res["mfma_frac"] = res["TFLOPs"] / PEAK_MFMA_TFLOPS[w.w_fmt]
+    res["mfma_frac"] = res["TFLOPs"] / mfma_peak(w)
     gu_ms = stages["gate_up"]
     decode = w.slots < 16 * (w.E + 1)
     if decode:   # decode sizes: the same steps replayed from HIP graphs
@@ -235,7 +242,7 @@ def measure(name, steps, warmup):
                            "bytes_per_launch": gate_up_bytes(w, touched)}
     else:
         ach = gate_up_flops(w) / (gu_ms * 1e-3) / 1e12
-        pk = PEAK_MFMA_TFLOPS[w.w_fmt]
+        pk = mfma_peak(w)
         res["roofline"] = {"kernel": "gate_up", "bound": "mfma", "achieved": ach, "peak": pk,
                            "unit": "TFLOP/s", "frac": ach / pk, "flops_per_launch": gate_up_flops(w)}
     log(f"{name}: {ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
@@ -365,7 +372,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_mxfp8")
     ap.add_argument("--extra", default="prefill_mxfp8,decode_mxfp4,wide512_mxfp4_T1,"
-                                       "wide512_mxfp4_T6,wide512_mxfp4_T4096",
+                                       "wide512_mxfp4_T6,wide512_mxfp4_T4096,decode_w4a4,"
+                                       "wide512_w4a4_T4096",
                     help="comma-separated extra workloads, 'all', or 'none'")
     ap.add_argument("--cpu-tokens", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -407,7 +415,11 @@ def main():
         others[n] = r
         del gx
         torch.cuda.empty_cache()
-    gate = {n: measure_gate(n) for n in [args.workload] + extra}
+    gate_shapes = {}
+    for n in [args.workload] + extra:   # one gate measurement per (T, H, E)
+        wn = workloads.get(n)
+        gate_shapes.setdefault((wn.T, wn.H, wn.E), n)
+    gate = {n: measure_gate(n) for n in gate_shapes.values()}
     rl = dict(head["roofline"])
     rl["traffic"] = traffic_record(args.workload,
                                    os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"))
@@ -416,7 +428,7 @@ def main():
         "metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"mxfp8": "mxfp8xmxfp8->f32", "mxfp4": "mxfp4xmxfp8->f32", "bf16": "bf16->f32"}[w.w_fmt],
+        "dtype": "bf16->f32" if w.w_fmt == "bf16" else f"{w.w_fmt}x{w.act_fmt}->f32",
         "data": "synthetic (seeded draws; weights N(0,0.02) quantised on the GPU)",
         "config": {"workload": args.workload, **{k: head[k] for k in
                    ("T", "H", "E", "top_k", "shared_experts", "I", "w_fmt", "act_fmt", "zipf")},

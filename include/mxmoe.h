@@ -66,11 +66,13 @@ enum { MXMOE_COMBINE_AUTO = 0, MXMOE_COMBINE_SLOTS = 1, MXMOE_COMBINE_ATOMIC = 2
        MXMOE_COMBINE_SLOTS_BF16 = 3 };
 
 /* Problem shape. Requirements: T >= 0; H % 128 == 0; I % 32 == 0; 1 <= top_k <= E <= 1024;
-   w_fmt in {BF16, MXFP8_E4M3, MXFP4_E2M1}; act_fmt = MXFP8_E4M3 for MX weights and BF16 for bf16
-   weights; logits_dtype in {BF16, F32}. The kernels address each of these with 32-bit offsets, so
-   each must stay below 2 GiB, or the call returns MXMOE_EUNSUPPORTED: one expert's W13 codes,
-   the activation codes (T*H bytes, 2*T*H for bf16) and the intermediate (about
-   T*(top_k+1)*I bytes plus tile padding, twice that for bf16). */
+   w_fmt in {BF16, MXFP8_E4M3, MXFP4_E2M1}; act_fmt = BF16 for bf16 weights, MXFP8_E4M3 for MX
+   weights, or MXFP4_E2M1 with MXFP4_E2M1 weights (W4A4: the activations and the SwiGLU
+   intermediate are quantised to MXFP4 and both MFMA operands are E2M1); logits_dtype in
+   {BF16, F32}. The kernels address each of these with 32-bit offsets, so each must stay below
+   2 GiB, or the call returns MXMOE_EUNSUPPORTED: one expert's W13 codes, the activation codes
+   (T*H bytes; T*H/2 for MXFP4, 2*T*H for bf16) and the intermediate (about T*(top_k+1)*I bytes
+   plus tile padding; half that for MXFP4, twice for bf16). */
 typedef struct {
   int32_t T, H, E, top_k, I;
   int32_t w_fmt, act_fmt, logits_dtype;
@@ -92,9 +94,9 @@ typedef struct {
      after it. NULL = no events. */
   void** stage_events;
   /* The whole block in one launch for small batches (routing, layout, gate_up, down and the final
-     sum as roles of one grid; small-M plan with 16-row tiles and fp32 slot rows): 0 = the
-     library's choice, 1 = required (MXMOE_EUNSUPPORTED if the shape or the other options do not
-     allow it), -1 = never. */
+     sum as roles of one grid; small-M plan with 16-row tiles and fp32 slot rows; MX weights with
+     MXFP8 activations, up to 128 tokens): 0 = the library's choice, 1 = required
+     (MXMOE_EUNSUPPORTED if the shape or the other options do not allow it), -1 = never. */
   int32_t fused;
   /* One-launch path: polls of a bounded wait before it gives up (0 = the default, about 50 ms).
      A wait that gives up skips the work that depended on it, every workgroup still ends, and the

@@ -39,9 +39,13 @@ class Shape(ctypes.Structure):
                 ("act_fmt", ctypes.c_int32), ("logits_dtype", ctypes.c_int32)]
 
     @staticmethod
-    def of(T, H, E, top_k, I, w_fmt="mxfp8", logits_dtype="bf16") -> "Shape":
+    def of(T, H, E, top_k, I, w_fmt="mxfp8", logits_dtype="bf16", act_fmt=None) -> "Shape":
+        """act_fmt None: bf16 activations for bf16 weights, MXFP8 for MX weights."""
         wf = FMT_BY_NAME[w_fmt] if isinstance(w_fmt, str) else int(w_fmt)
-        af = MXMOE_BF16 if wf == MXMOE_BF16 else MXMOE_MXFP8_E4M3
+        if act_fmt is None:
+            af = MXMOE_BF16 if wf == MXMOE_BF16 else MXMOE_MXFP8_E4M3
+        else:
+            af = FMT_BY_NAME[act_fmt] if isinstance(act_fmt, str) else int(act_fmt)
         ld = FMT_BY_NAME[logits_dtype] if isinstance(logits_dtype, str) else int(logits_dtype)
         return Shape(T, H, E, top_k, I, wf, af, ld)
 

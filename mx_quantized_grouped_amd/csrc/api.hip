@@ -84,7 +84,11 @@ int check_shape(const mxmoe_shape* s) {
   if (s->logits_dtype != MXMOE_BF16 && s->logits_dtype != MXMOE_F32) return MXMOE_EINVAL;
   bool mxw = s->w_fmt == MXMOE_MXFP8_E4M3 || s->w_fmt == MXMOE_MXFP4_E2M1;
   if (!mxw && s->w_fmt != MXMOE_BF16) return MXMOE_EINVAL;
-  if (mxw && s->act_fmt != MXMOE_MXFP8_E4M3) return MXMOE_EUNSUPPORTED;
+  // MX weights take MXFP8 activations; MXFP4 weights also MXFP4 activations (both MFMA operands
+  // E2M1)
+  if (mxw && s->act_fmt != MXMOE_MXFP8_E4M3 &&
+      !(s->w_fmt == MXMOE_MXFP4_E2M1 && s->act_fmt == MXMOE_MXFP4_E2M1))
+    return MXMOE_EUNSUPPORTED;
   if (!mxw && s->act_fmt != MXMOE_BF16) return MXMOE_EUNSUPPORTED;
   // one expert's prepacked W13 (W2 is half of it) is addressed with 32-bit offsets
   const double eb = s->w_fmt == MXMOE_MXFP8_E4M3 ? 1.0 : (s->w_fmt == MXMOE_MXFP4_E2M1 ? 0.5 : 2.0);
@@ -104,6 +108,7 @@ struct Plan {
   int combine;  // 1 slots, 2 atomic, 3 bf16 slots
   bool fuse_final;  // final bf16 rounding inside the down pass (small M, atomic combine)
   int bm, cap, Ip, srs_H, srs_I;
+  int xrow, hrow;  // bytes of an activation-code row [H] and of an intermediate row [Ip]
   int unit_run;  // large-M unit order from the options (0 = the launcher's default)
   bool fused;    // the one-launch path (small batches)
   int spin_limit, hold;
@@ -113,12 +118,12 @@ struct Plan {
 // Every buffer the kernels address with 32-bit offsets stays below 2 GiB: activation codes and
 // scales, the intermediate and its scales, and one expert's prepacked weights (the descriptors'
 // range and the row offsets are 32-bit; the out-of-range sentinel 0x80000000 must not be valid).
-bool within_offsets(const mxmoe_shape* s, int T, int cap, int Ip, int srs_H, int srs_I, bool mx) {
+bool within_offsets(const Plan& p) {
   const size_t lim = kMaxBufferBytes;
-  if ((size_t)T * s->H * (mx ? 1 : 2) >= lim) return false;
-  if ((size_t)T * srs_H >= lim) return false;
-  if ((size_t)cap * Ip * (mx ? 1 : 2) >= lim) return false;
-  if ((size_t)cap * srs_I >= lim) return false;
+  if ((size_t)p.T * p.xrow >= lim) return false;
+  if ((size_t)p.T * p.srs_H >= lim) return false;
+  if ((size_t)p.cap * p.hrow >= lim) return false;
+  if ((size_t)p.cap * p.srs_I >= lim) return false;
   return true;
 }
 
@@ -134,6 +139,7 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.T = s->T; p.H = s->H; p.E = s->E; p.k = s->top_k; p.I = s->I;
   p.k1 = p.k + 1; p.S = p.T * p.k1; p.E1 = p.E + 1;
   p.wf = wf_of(s->w_fmt);
+  if (p.wf == WF_FP4 && s->act_fmt == MXMOE_MXFP4_E2M1) p.wf = WF_FP4A4;
   p.mx = p.wf != WF_BF16;
   // Launcher: block-major (large-M) once the average expert holds enough rows to fill tiles.
   p.large = o.launcher == MXMOE_LAUNCH_LARGE_M ||
@@ -161,8 +167,10 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.Ip = round_up(p.I, KSTEP);
   p.srs_H = scale_row_bytes(p.H);
   p.srs_I = scale_row_bytes(p.Ip);
+  p.xrow = !p.mx ? 2 * p.H : (a_is_fp4(p.wf) ? p.H / 2 : p.H);
+  p.hrow = !p.mx ? 2 * p.Ip : (a_is_fp4(p.wf) ? p.Ip / 2 : p.Ip);
   p.unit_run = o.unit_run;
-  if (!within_offsets(s, p.T, p.cap, p.Ip, p.srs_H, p.srs_I, p.mx)) return MXMOE_EUNSUPPORTED;
+  if (!within_offsets(p)) return MXMOE_EUNSUPPORTED;
   size_t sz[NSEG];
   sz[SEG_CTL] = kFusedCtlBytes;  // first in every plan, so any call may follow any other
   sz[SEG_IDS] = (size_t)p.S * 4;
@@ -173,9 +181,9 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   sz[SEG_EXPOFF] = (size_t)(p.E1 + 1) * 4;
   sz[SEG_TOUCHED] = (size_t)p.E1 * 4;
   sz[SEG_ALIGN] = align_scratch_bytes(p.T, p.E, p.k);
-  sz[SEG_XQ] = p.mx ? (size_t)p.T * p.H : 0;
+  sz[SEG_XQ] = p.mx ? (size_t)p.T * p.xrow : 0;
   sz[SEG_XS] = p.mx ? (size_t)p.T * p.srs_H : 0;
-  sz[SEG_H] = (size_t)p.cap * p.Ip * (p.mx ? 1 : 2);
+  sz[SEG_H] = (size_t)p.cap * p.hrow;
   sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
   sz[SEG_DONE] = p.fuse_final ? (size_t)(p.H / 64) * 4 : 0;
   sz[SEG_SORTW] = (size_t)p.cap * 4;
@@ -330,8 +338,8 @@ size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int 
   if (which < 0 || which >= MXMOE_VIEW_COUNT) return (size_t)-1;
   const size_t sz[MXMOE_VIEW_COUNT] = {
       (size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4, (size_t)(p.cap / p.bm) * 4, 4,
-      (size_t)(p.E1 + 1) * 4, p.mx ? (size_t)p.T * p.H : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
-      (size_t)p.cap * p.Ip * (p.mx ? 1 : 2), p.mx ? (size_t)p.cap * p.srs_I : 0, 4};
+      (size_t)(p.E1 + 1) * 4, p.mx ? (size_t)p.T * p.xrow : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
+      (size_t)p.cap * p.hrow, p.mx ? (size_t)p.cap * p.srs_I : 0, 4};
   if (bytes) *bytes = sz[which];
   if (block_m) *block_m = p.bm;
   return p.off[segs[which]] + (which == MXMOE_VIEW_STATUS ? kFusedStatusByte : 0);
@@ -426,6 +434,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   pa.H = P.H;
   pa.xq = P.mx ? xq : nullptr;
   pa.xs = xs;
+  pa.a4 = a_is_fp4(P.wf);
   pa.srs = P.srs_H;
   pa.zero_out = slots ? nullptr : out32;
   pa.zero_cnt = P.fuse_final ? done : nullptr;
@@ -447,7 +456,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.H = P.H;
   g.h = h;
   g.hs = hs;
-  g.h_stride = P.Ip * (P.mx ? 1 : 2);
+  g.h_stride = P.hrow;
   g.h_srs = P.srs_I;
   g.topk_w = tw;
   g.sorted_w = sorted_w;
@@ -465,7 +474,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     GemmParams gu = g;
     gu.a = P.mx ? xq : (const uint8_t*)x;
     gu.as = xs;
-    gu.a_stride = P.mx ? P.H : 2 * P.H;
+    gu.a_stride = P.xrow;
     gu.a_srs = P.srs_H;
     gu.a_bytes = (uint32_t)((size_t)P.T * gu.a_stride);
     gu.as_bytes = (uint32_t)((size_t)P.T * P.srs_H);

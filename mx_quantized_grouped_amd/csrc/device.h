@@ -13,8 +13,12 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // K elements consumed by one block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
 constexpr int KSTEP = 128;
-// Weight formats of the B operand.
-enum WFmt { WF_FP8 = 0, WF_FP4 = 1, WF_BF16 = 2 };
+// Operand formats of a grouped GEMM: the weight (B) element, and for the MX formats the
+// activation (A) element: MXFP8 weights and activations, MXFP4 weights with MXFP8 activations,
+// bf16 both, and MXFP4 weights with MXFP4 activations (W4A4).
+enum WFmt { WF_FP8 = 0, WF_FP4 = 1, WF_BF16 = 2, WF_FP4A4 = 3 };
+__host__ __device__ constexpr bool w_is_fp4(int wf) { return wf == WF_FP4 || wf == WF_FP4A4; }
+__host__ __device__ constexpr bool a_is_fp4(int wf) { return wf == WF_FP4A4; }
 
 // ---------------------------------------------------------------------------- lane helpers
 __device__ __forceinline__ int lane_id() {
@@ -79,6 +83,17 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, int se) {
   float v = ldexpf(x, -se);
   uint32_t m = e2m1_mag(fminf(fabsf(v), 6.0f));
   return m | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// E2M1 codes of columns n and 16 + n of a 32-column MX block whose 16 columns pairs are spread over
+// the 16 lanes of a DPP row (lane n holds columns n and 16 + n), packed two codes per byte,
+// element 2i in the low nibble: an even lane n returns byte n / 2 (columns n, n + 1) in bits 0-7
+// and byte 8 + n / 2 (columns 16 + n, 17 + n) in bits 8-15. All 64 lanes must take part.
+__device__ __forceinline__ uint32_t e2m1_pack_pair(float a0, float a1, int se) {
+  const uint32_t q = e2m1_code(a0, se) | (e2m1_code(a1, se) << 8);
+  // quad_perm [1,0,3,2]: the codes of the neighbouring column pair
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)q, (int)q, 0xB1, 0xF, 0xF, false);
+  return (q & 0x0F0Fu) | ((nb & 0x0F0Fu) << 4);
 }
 
 // ---------------------------------------------------------------------------- layouts

@@ -727,7 +727,7 @@ constexpr int kFusedSplitMaxUnits = 1024;
 }  // namespace
 
 bool fused_fits(int wf, int T, int H, int E, int top_k, int I) {
-  if (wf == WF_BF16 || T < 1) return false;
+  if (wf == WF_BF16 || a_is_fp4(wf) || T < 1) return false;
   const int S = T * (top_k + 1);
   if (T > kFusedMaxT || S > kAlignSmallMaxSlots) return false;
   if ((E + 1) * ((S + 63) / 64) > kFusedBitmapWords) return false;

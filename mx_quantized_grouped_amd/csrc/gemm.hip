@@ -40,7 +40,19 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
       const int rr = m0 + 16 * mt + 4 * g + i;
       float a0 = silu(acc[mt][0][i]) * acc[mt][1][i];
       float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
-      if (WF != WF_BF16) {
+      if (a_is_fp4(WF)) {  // E2M1 intermediate: 16 bytes per 32 columns, two codes per byte
+        const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
+        const int se = mx_shared_exp<2>(m);
+        const uint32_t b2 = e2m1_pack_pair(a0, a1, se);
+        if (rr < r1) {
+          uint8_t* hr = p.h + (size_t)rr * p.h_stride + ic0 / 2;
+          if (!(n & 1)) {
+            hr[n / 2] = (uint8_t)b2;
+            hr[8 + n / 2] = (uint8_t)(b2 >> 8);
+          }
+          if (n == 0) p.hs[(size_t)rr * p.h_srs + chunk] = (uint8_t)(se + 127);
+        }
+      } else if (WF != WF_BF16) {
         const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
         int se = mx_shared_exp<8>(m);
         if (rr < r1) {
@@ -64,7 +76,8 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
         const int rr = m0 + 16 * mt + 4 * g + i;
         if (rr >= r1) continue;
         if (WF != WF_BF16) {
-          for (int c = p.I + n; c < p.Ip; c += 16) p.h[(size_t)rr * p.h_stride + c] = 0;
+          const int cb = a_is_fp4(WF) ? 2 : 1;  // codes per byte
+          for (int c = p.I / cb + n; c < p.Ip / cb; c += 16) p.h[(size_t)rr * p.h_stride + c] = 0;
           if (n == 0)
             for (int kb = p.I / 32; kb < p.Ip / 32; ++kb)
               p.hs[(size_t)rr * p.h_srs + kb] = 127;
@@ -266,11 +279,17 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
 // CU and each one's load waits are covered by the other's MFMAs (measured on the 8K-token
 // prefill: gate_up 274 us, down 253 us, against 316 / 312 us for one workgroup per CU with every
 // operand staged through a three-deep LDS ring).
+// With E2M1 activations a row of the K-step is 64 bytes (four 16-byte units, one K-block each),
+// stored at pitch 64 with unit c of row r at c ^ a4_swz(r): reading 16 rows at one K-block then
+// takes each 16-byte slot of a 128-byte (and of a 256-byte) bank window once.
 // Stage completion is a wait on the wave's own load counter followed by a workgroup barrier,
 // written as one asm statement (the compiler's barrier would also wait for loads it cannot see).
 constexpr int kTileM = 128;
 constexpr int kTileWaves = 4;
 constexpr int kLdsPitch = KSTEP;
+
+// Unit swizzle of an E2M1 activation row in LDS (r & 15 = the row within its 16-row group).
+__device__ __forceinline__ int a4_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Raw buffer descriptor words (same format as raw_rsrc) for the asm loads below.
 __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_bytes) {
@@ -303,11 +322,14 @@ __device__ __forceinline__ void wait_loads_barrier() {
 // code bytes go out as 16-byte stores (8 lanes per row) and its 4 scale bytes as one dword (the
 // scale layout is in K-block order). Rows of padding slots are written too (their codes are zero
 // since their activation rows read as zero), so the down pass can read every row of a tile.
+// With E2M1 intermediates (a_is_fp4) a row of the tile is 64 code bytes, two codes per byte.
 template <int WF, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const v4f (&acc)[8][4],
                                                       int r0, int chunk, int wave, int n, int g,
                                                       int tid, uint8_t* lds) {
-  constexpr int kPitch = 128 + 16;           // code row pitch in LDS
+  constexpr bool A4 = a_is_fp4(WF);
+  constexpr int kRowBytes = A4 ? 64 : 128;   // code bytes of a row of the tile
+  constexpr int kPitch = kRowBytes + 16;     // code row pitch in LDS
   static_assert(kTileM * kPitch + kTileM * 4 <= LDS_BYTES, "gate_up staging exceeds the LDS buffer");
   uint8_t* codes = lds;                      // [128][kPitch]
   uint32_t* scales = (uint32_t*)(lds + kTileM * kPitch);  // [128] dwords, byte = wave
@@ -319,18 +341,29 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
       const float a0 = silu(acc[mt][0][i]) * acc[mt][1][i];
       const float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
       const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
-      const int se = mx_shared_exp<8>(m);
-      const uint32_t c2 = e4m3_pair(a0, a1, se);
-      codes[row * kPitch + 32 * wave + n] = (uint8_t)c2;
-      codes[row * kPitch + 32 * wave + 16 + n] = (uint8_t)(c2 >> 8);
-      if (n == 0) ((uint8_t*)scales)[4 * row + wave] = (uint8_t)(se + 127);
+      if constexpr (A4) {
+        const int se = mx_shared_exp<2>(m);
+        const uint32_t b2 = e2m1_pack_pair(a0, a1, se);
+        if (!(n & 1)) {
+          codes[row * kPitch + 16 * wave + n / 2] = (uint8_t)b2;
+          codes[row * kPitch + 16 * wave + 8 + n / 2] = (uint8_t)(b2 >> 8);
+        }
+        if (n == 0) ((uint8_t*)scales)[4 * row + wave] = (uint8_t)(se + 127);
+      } else {
+        const int se = mx_shared_exp<8>(m);
+        const uint32_t c2 = e4m3_pair(a0, a1, se);
+        codes[row * kPitch + 32 * wave + n] = (uint8_t)c2;
+        codes[row * kPitch + 32 * wave + 16 + n] = (uint8_t)(c2 >> 8);
+        if (n == 0) ((uint8_t*)scales)[4 * row + wave] = (uint8_t)(se + 127);
+      }
     }
   }
   __syncthreads();
+  constexpr int kUnits = kRowBytes / 16;     // 16-byte stores per row
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + 256 * j, row = c >> 3, unit = c & 7;
-    *(v4i*)(p.h + (size_t)(r0 + row) * p.h_stride + 128 * chunk + 16 * unit) =
+  for (int j = 0; j < kTileM * kUnits / 256; ++j) {
+    const int c = tid + 256 * j, row = c / kUnits, unit = c % kUnits;
+    *(v4i*)(p.h + (size_t)(r0 + row) * p.h_stride + kRowBytes * chunk + 16 * unit) =
         *(const v4i*)(codes + row * kPitch + 16 * unit);
   }
   if (tid < kTileM)
@@ -443,18 +476,31 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
     }
     return (uint32_t)r * stride;
   };
-  uint32_t aoff[4];
+  // Per wave and K-step, 32 activation rows: E4M3 rows of 128 bytes in 4 loads of 8 rows, E2M1
+  // rows of 64 bytes in 2 loads of 16 rows (lane: row lane / 4, unit lane % 4).
+  constexpr bool A4 = a_is_fp4(WF);
+  constexpr int kAPitch = A4 ? KSTEP / 2 : kLdsPitch;  // LDS (and global per-step) row bytes
+  constexpr int kALoads = A4 ? 2 : 4;
+  constexpr int kARows = 32 / kALoads;                 // rows per load
+  uint32_t aoff[kALoads];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    aoff[j] = act_row(r0 + 32 * wave + 8 * j + (lane >> 3), (uint32_t)p.a_stride) +
-              16u * ((lane & 7) ^ (lane >> 3));
+  for (int j = 0; j < kALoads; ++j) {
+    if constexpr (A4) {
+      const int lr = lane >> 2;
+      aoff[j] = act_row(r0 + 32 * wave + kARows * j + lr, (uint32_t)p.a_stride) +
+                16u * ((lane & 3) ^ a4_swz(lr));
+    } else {
+      aoff[j] = act_row(r0 + 32 * wave + kARows * j + (lane >> 3), (uint32_t)p.a_stride) +
+                16u * ((lane & 7) ^ (lane >> 3));
+    }
+  }
   const uint32_t asoff = wave < 2 ? act_row(r0 + 64 * wave + lane, (uint32_t)p.a_srs) : kOutOfRange;
   const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
   auto issue_a = [&](int stage, int ks, uint32_t oob) {
     const uint32_t st = lds0 + stage * L::bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      lds_load16(ra, st + L::a + (32 * wave + 8 * j) * kLdsPitch, aoff[j] | oob, ks * KSTEP);
+    for (int j = 0; j < kALoads; ++j)
+      lds_load16(ra, st + L::a + (32 * wave + kARows * j) * kAPitch, aoff[j] | oob, ks * kAPitch);
     lds_load4(ras, st + L::as + 256 * wave, asoff | oob, 4 * ks);
   };
   v4f acc[MT][4];
@@ -462,17 +508,24 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int u0 = (g ^ (n & 7)) << 4, u1 = ((4 + g) ^ (n & 7)) << 4;
+  const int u0 = A4 ? (g ^ a4_swz(n)) << 4 : (g ^ (n & 7)) << 4;
+  const int u1 = ((4 + g) ^ (n & 7)) << 4;
   Stage<WF, 1> bs[2];
-  auto compute = [&](int stage, const Stage<WF, 1>& b, int mt0, int mt1) {
+  // The lane's A fragment of 16-row group mt: two 16-byte units (E4M3) or one (E2M1, the upper
+  // half of the operand is zero) and the row's scale dword.
+  auto a_frag = [&](int stage, int mt, v8i& a8, uint32_t& sa) {
     const uint8_t* st = lds + stage * L::bytes;
-    const uint8_t* base = st + L::a + n * kLdsPitch;
+    const uint8_t* base = st + L::a + n * kAPitch;
+    a8.lo = *(const v4i*)(base + mt * 16 * kAPitch + u0);
+    a8.hi = A4 ? v4i{0, 0, 0, 0} : *(const v4i*)(base + mt * 16 * kAPitch + u1);
+    sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
+  };
+  auto compute = [&](int stage, const Stage<WF, 1>& b, int mt0, int mt1) {
 #pragma unroll
     for (int mt = mt0; mt < mt1; ++mt) {
       v8i a8;
-      a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
-      a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
-      const uint32_t sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
+      uint32_t sa;
+      a_frag(stage, mt, a8, sa);
       mma_frags<WF>(a8, (int)(sa >> (8 * g)), b.b, (int)b.sb, acc[mt]);
     }
   };
@@ -491,13 +544,6 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   // PIPE: the next step's weights go out first, so they have a whole step to arrive, and the
   // activation fragments are read one 16-row group ahead of their MFMAs (two register sets).
   // PRIO: the wave's priority is raised while it issues the step's MFMAs.
-  auto a_frag = [&](int stage, int mt, v8i& a8, uint32_t& sa) {
-    const uint8_t* st = lds + stage * L::bytes;
-    const uint8_t* base = st + L::a + n * kLdsPitch;
-    a8.lo = *(const v4i*)(base + mt * 16 * kLdsPitch + u0);
-    a8.hi = *(const v4i*)(base + mt * 16 * kLdsPitch + u1);
-    sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
-  };
   auto step_pipe = [&](auto SLOT, int ks) {
     constexpr int s = decltype(SLOT)::value;
     const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
@@ -616,7 +662,7 @@ inline bool tile_prio(bool gate_up) {
 
 inline bool tile_pipe(bool gate_up, int wf) {
   if (tuning().tile_pipe >= 0) return tuning().tile_pipe != 0;
-  return gate_up || wf == WF_FP4;
+  return gate_up || w_is_fp4(wf);
 }
 
 template <int WF, bool GATE_UP, int D, int KS = 1>
@@ -687,6 +733,7 @@ hipError_t launch_wf(int wf, bool large, const GemmParams& p, int n_blocks, hipS
   switch (wf) {
     case WF_FP8: return launch_one<WF_FP8, GATE_UP>(large, p, n_blocks, st);
     case WF_FP4: return launch_one<WF_FP4, GATE_UP>(large, p, n_blocks, st);
+    case WF_FP4A4: return launch_one<WF_FP4A4, GATE_UP>(large, p, n_blocks, st);
     default: return launch_one<WF_BF16, GATE_UP>(large, p, n_blocks, st);
   }
 }

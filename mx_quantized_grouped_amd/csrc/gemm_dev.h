@@ -19,6 +19,7 @@ template <int WF> struct Frag;
 template <> struct Frag<WF_FP8> { static constexpr int bytes = 2048; };
 template <> struct Frag<WF_FP4> { static constexpr int bytes = 1024; };
 template <> struct Frag<WF_BF16> { static constexpr int bytes = 4096; };
+template <> struct Frag<WF_FP4A4> { static constexpr int bytes = 1024; };
 
 // Operands of one 128-K step for one wave: 4 weight fragments and MT activation fragments.
 template <int WF, int MT>
@@ -61,7 +62,7 @@ struct TileRows {
 // Weight and activation descriptors of the wave's tile (expert e, first fragment nt0).
 template <int WF, int MT>
 __device__ __forceinline__ void tile_weights(const GemmParams& p, int e, int nt0, TileRows<MT>& tr) {
-  constexpr int FB = WF == WF_FP8 ? 2048 : (WF == WF_FP4 ? 1024 : 4096);
+  constexpr int FB = Frag<WF>::bytes;
   const size_t wbytes = (size_t)p.NT * p.NKS * FB;
   tr.w = raw_rsrc(p.w + (size_t)e * wbytes, (uint32_t)wbytes);
   if (WF != WF_BF16) {
@@ -117,7 +118,7 @@ __device__ __forceinline__ void load_b(const GemmParams& p, const TileRows<MTR>&
     if (WF == WF_FP8) {
       s.b[f][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.w, vo, soff, AUX);
       s.b[f][1] = __builtin_amdgcn_raw_buffer_load_b128(tr.w, vo + 1024u, soff, AUX);
-    } else if (WF == WF_FP4) {
+    } else if (w_is_fp4(WF)) {
       s.b[f][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.w, vo, soff, AUX);
     } else {
 #pragma unroll
@@ -133,7 +134,10 @@ template <int WF, int MT>
 __device__ __forceinline__ void load_a(const TileRows<MT>& tr, int ks, Stage<WF, MT>& s) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    if (WF != WF_BF16) {
+    if (a_is_fp4(WF)) {  // one K-block (32 codes, 16 bytes) per lane; rows of 64 bytes per step
+      s.a[mt][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, tr.aoff[mt], ks * (KSTEP / 2), 0);
+      s.sa[mt] = __builtin_amdgcn_raw_buffer_load_b32(tr.as, tr.asoff[mt], 4 * ks, 0);
+    } else if (WF != WF_BF16) {
       s.a[mt][0] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, tr.aoff[mt], ks * KSTEP, 0);
       s.a[mt][1] = __builtin_amdgcn_raw_buffer_load_b128(tr.a, tr.aoff[mt] + 64u, ks * KSTEP, 0);
       s.sa[mt] = __builtin_amdgcn_raw_buffer_load_b32(tr.as, tr.asoff[mt], 4 * ks, 0);
@@ -154,7 +158,9 @@ __device__ __forceinline__ void load_stage(const GemmParams& p, const TileRows<M
 }
 
 // The four block-scaled MFMAs of one A fragment against the wave's 4 weight fragments; the scale
-// operand of fragment F is byte F of sb (selected by the instruction's op_sel).
+// operand of fragment F is byte F of sb (selected by the instruction's op_sel). The element
+// formats go in the instruction's cbsz (A) and blgp (B) fields: 0 E4M3, 4 E2M1; an E2M1 operand
+// is 32 codes in the low four dwords of the lane.
 template <int WF, int F = 0>
 __device__ __forceinline__ void mma_frags(const v8i& a8, int sa, const v4i (&b)[4][2], int sb,
                                           v4f (&acc)[4]) {
@@ -162,8 +168,8 @@ __device__ __forceinline__ void mma_frags(const v8i& a8, int sa, const v4i (&b)[
     v8i b8;
     b8.lo = b[F][0];
     b8.hi = (WF == WF_FP8) ? b[F][1] : v4i{0, 0, 0, 0};
-    acc[F] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[F], 0,
-                                                              WF == WF_FP4 ? 4 : 0, 0, sa, F, sb);
+    acc[F] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        a8, b8, acc[F], a_is_fp4(WF) ? 4 : 0, w_is_fp4(WF) ? 4 : 0, 0, sa, F, sb);
     mma_frags<WF, F + 1>(a8, sa, b, sb, acc);
   }
 }
@@ -176,7 +182,7 @@ __device__ __forceinline__ void mma_stage(const Stage<WF, MT>& s, int ash, v4f (
     if constexpr (WF != WF_BF16) {
       v8i a8;
       a8.lo = s.a[mt][0];
-      a8.hi = s.a[mt][1];
+      a8.hi = a_is_fp4(WF) ? v4i{0, 0, 0, 0} : s.a[mt][1];
       mma_frags<WF>(a8, (int)(s.sa[mt] >> ash), s.b, (int)s.sb, acc[mt]);
     } else {
 #pragma unroll

@@ -70,6 +70,7 @@ struct PrologueArgs {
   int H;
   uint8_t* xq;      // null: no quantisation (bf16 path)
   uint8_t* xs;
+  bool a4;          // E2M1 activation codes (rows of H / 2 bytes), else E4M3 (rows of H bytes)
   int srs;
   float* zero_out;  // null: nothing to clear
   int32_t* zero_cnt;  // n_cnt counters to clear (null: none)
@@ -82,11 +83,6 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
 // Canonical MX quantisation (codes row-major, scales [rows, K/32]).
 hipError_t launch_quantize_canonical(const void* src, bool src_f32, int rows, int K, bool fp4,
                                      uint8_t* codes, uint8_t* scales, hipStream_t st);
-// Activation rows -> MXFP8 in the kernel-native layout (codes [T, H], scales [T, srs]); when
-// zero_out != nullptr also clears zero_out[T, H] (fp32), the atomic-combine accumulator.
-hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs,
-                               int srs, float* zero_out, hipStream_t st);
-hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
 
 // prepack.hip
 struct PrepackDims {

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
   const int nbk = a.H / 32;
   if (blk >= (size_t)a.T * nbk) return;
   const size_t t = blk / nbk;
-  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.zero_out);
+  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.a4, a.zero_out);
 }
 
 // Larger batches: workgroups [0, n_route) route 16 tokens each; the rest quantise / clear.
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_
   const int nbk = a.H / 32;
   if (blk >= (size_t)a.T * nbk) return;
   const size_t t = blk / nbk;
-  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.zero_out);
+  quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.a4, a.zero_out);
 }
 
 }  // namespace

@@ -41,22 +41,6 @@ __global__ __launch_bounds__(256) void k_quant_canonical(const void* src, int ro
   }
 }
 
-// Activations: bf16 x [T, H] -> E4M3 codes [T, H] + kernel-native scales [T, srs].
-__global__ __launch_bounds__(256) void k_quant_act(const uint16_t* x, int T, int H, uint8_t* xq,
-                                                   uint8_t* xs, int srs, float* zero_out) {
-  const int nbk = H / 32;
-  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t blk = g >> 2;  // four lanes per block
-  if (blk >= (size_t)T * nbk) return;
-  const size_t t = blk / nbk;
-  quant_act_part(x, t, (int)(blk - t * nbk), (int)(g & 3), H, xq, xs, srs, zero_out);
-}
-
-__global__ __launch_bounds__(256) void k_zero_f32(float* p, size_t n) {
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
-
 }  // namespace
 
 hipError_t launch_quantize_canonical(const void* src, bool src_f32, int rows, int K, bool fp4,
@@ -71,21 +55,6 @@ hipError_t launch_quantize_canonical(const void* src, bool src_f32, int rows, in
     if (fp4) hipLaunchKernelGGL((k_quant_canonical<false, true>), grid, block, 0, st, src, rows, K, codes, scales);
     else hipLaunchKernelGGL((k_quant_canonical<false, false>), grid, block, 0, st, src, rows, K, codes, scales);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs,
-                               int srs, float* zero_out, hipStream_t st) {
-  size_t nblk = (size_t)T * (H / 32);
-  if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)((4 * nblk + 255) / 256)), dim3(256), 0, st, x,
-                     T, H, xq, xs, srs, zero_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

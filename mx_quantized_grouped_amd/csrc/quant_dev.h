@@ -54,15 +54,15 @@ __device__ __forceinline__ void encode_fp4_32(const float* v, int se, uint32_t* 
   }
 }
 
-// Activation block (t, kb) of bf16 x [T, H] -> E4M3 codes in xq [T, H] and the scale byte in
-// xs [T, srs] (K-block order); optionally clears the matching 32 floats of zero_out [T, H]. Four
-// consecutive lanes (a DPP quad) share a block, lane part p holding elements 8p .. 8p + 7, so each
-// load instruction of a wave reads 1 KiB of consecutive bytes and each store writes consecutive
-// bytes (one thread per block read 16-byte pieces 64 bytes apart: the 8K-token quantisation ran at
-// ~3 TB/s). The block maximum is exact whatever the order, so the codes are those of the
-// one-thread-per-block rule.
+// Activation block (t, kb) of bf16 x [T, H] -> E4M3 codes in xq [T, H] (A4: E2M1 codes, two per
+// byte, in xq [T, H / 2]) and the scale byte in xs [T, srs] (K-block order); optionally clears the
+// matching 32 floats of zero_out [T, H]. Four consecutive lanes (a DPP quad) share a block, lane
+// part p holding elements 8p .. 8p + 7, so each load instruction of a wave reads 1 KiB of
+// consecutive bytes and each store writes consecutive bytes (one thread per block read 16-byte
+// pieces 64 bytes apart: the 8K-token quantisation ran at ~3 TB/s). The block maximum is exact
+// whatever the order, so the codes are those of the one-thread-per-block rule.
 __device__ __forceinline__ void quant_act_part(const uint16_t* x, size_t t, int kb, int part,
-                                               int H, uint8_t* xq, uint8_t* xs, int srs,
+                                               int H, uint8_t* xq, uint8_t* xs, int srs, bool a4,
                                                float* zero_out) {
   const size_t off = t * H + (size_t)kb * 32 + 8 * part;
   if (xq) {
@@ -80,10 +80,19 @@ __device__ __forceinline__ void quant_act_part(const uint16_t* x, size_t t, int 
     // quad_perm [1,0,3,2], then [2,3,0,1]: the maximum over the block's four lanes
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0xB1, 0xF, 0xF, false)));
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x4E, 0xF, 0xF, false)));
-    const int se = mx_shared_exp<8>(m);
-    if (part == 0) xs[t * srs + kb] = (uint8_t)(se + 127);
-    *(uint2*)(xq + off) = uint2{e4m3_quad(v[0], v[1], v[2], v[3], se),
-                                e4m3_quad(v[4], v[5], v[6], v[7], se)};
+    if (a4) {
+      const int se = mx_shared_exp<2>(m);
+      if (part == 0) xs[t * srs + kb] = (uint8_t)(se + 127);
+      uint32_t d = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d |= e2m1_code(v[j], se) << (4 * j);
+      *(uint32_t*)(xq + off / 2) = d;
+    } else {
+      const int se = mx_shared_exp<8>(m);
+      if (part == 0) xs[t * srs + kb] = (uint8_t)(se + 127);
+      *(uint2*)(xq + off) = uint2{e4m3_quad(v[0], v[1], v[2], v[3], se),
+                                  e4m3_quad(v[4], v[5], v[6], v[7], se)};
+    }
   }
   if (zero_out) {
     v4f* z = (v4f*)(zero_out + off);

@@ -24,7 +24,7 @@ def f64(bits: np.ndarray) -> np.ndarray:
 
 
 def shape_of(w: workloads.Workload, logits_dtype="bf16") -> B.Shape:
-    return B.Shape.of(w.T, w.H, w.E, w.top_k, w.I, w.w_fmt, logits_dtype)
+    return B.Shape.of(w.T, w.H, w.E, w.top_k, w.I, w.w_fmt, logits_dtype, w.act_fmt)
 
 
 def packed_weights(name: str):

@@ -173,6 +173,25 @@ def test_workspace_view(L):
         B.mxmoe_workspace_view(s, None, -1)
 
 
+def test_w4a4_plan(L):
+    # MXFP4 activations with MXFP4 weights: E2M1 activation codes and intermediate take half the
+    # bytes of E4M3 ones, with the same scale rows
+    s = B.Shape.of(128, 3072, 128, 8, 768, "mxfp4", act_fmt="mxfp4")
+    a8 = B.Shape.of(128, 3072, 128, 8, 768, "mxfp4")
+    assert B.mxmoe_workspace_bytes(s) > 0
+    assert B.mxmoe_workspace_view(s, None, B.VIEW_XQ)[1] == 128 * 3072 // 2
+    for v in (B.VIEW_XS, B.VIEW_HS, B.VIEW_SORTED_IDS):
+        assert B.mxmoe_workspace_view(s, None, v)[1] == B.mxmoe_workspace_view(a8, None, v)[1]
+    assert 2 * B.mxmoe_workspace_view(s, None, B.VIEW_H)[1] == B.mxmoe_workspace_view(a8, None, B.VIEW_H)[1]
+    pad = B.Shape.of(4, 256, 4, 2, 96, "mxfp4", act_fmt="mxfp4")     # K of down padded to 128
+    assert B.mxmoe_workspace_view(pad, None, B.VIEW_H)[1] == L.mxmoe_align_capacity(4, 4, 2, 16) * 64
+    # MXFP4 activations need MXFP4 weights; the one-launch path takes E4M3 activations only
+    for wf in (B.MXMOE_BF16, B.MXMOE_MXFP8_E4M3):
+        assert B.mxmoe_workspace_bytes(B.Shape(128, 3072, 128, 8, 768, wf, B.MXMOE_MXFP4_E2M1, 0)) == 0
+    assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, 0, None, 1)) == 0
+    assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, 0, None, -1)) > 0
+
+
 def test_options_one_launch(L):
     dec = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
     fused = B.Options(0, 0, 0, 0, None, 1)

@@ -13,8 +13,8 @@ an exact value and fails here, where the output tolerance alone might absorb it.
 
 Paths covered: the small-M streaming launcher (with split K over four waves at H = 512), the
 large-M tile launcher (128- and 256-row layout blocks), the one-wave large-M launcher (other tile
-heights, and the down pass when H/64 is not a multiple of 4), fp8, fp4 and bf16 weights, fp32
-slot rows and the atomic combine. bf16 slot rows (one rounding per slot) are not exact and are
+heights, and the down pass when H/64 is not a multiple of 4), fp8, fp4 and bf16 weights, MXFP4
+weights with MXFP4 activations and intermediate (W4A4), fp32 slot rows and the atomic combine. bf16 slot rows (one rounding per slot) are not exact and are
 covered by the tolerance tests."""
 import numpy as np
 import pytest
@@ -36,6 +36,8 @@ CASES = [  # T, H, E, top_k, I, weight format
     (300, 256, 4, 2, 128, "mxfp4"),
     (40, 384, 6, 4, 128, "mxfp8"),
     (20, 256, 8, 2, 128, "bf16"),
+    (24, 512, 8, 2, 256, "w4a4"),     # MXFP4 weights and activations
+    (300, 256, 4, 2, 128, "w4a4"),
 ]
 OPTIONS = [None, (1, 1, 0), (1, 2, 0), (2, 1, 0), (2, 2, 0), (2, 1, 32), (2, 1, 256), "one_launch"]
 
@@ -70,8 +72,9 @@ def case(request):
     _say("case", request.param)
     xb, lb, experts = workloads.draw_exact_block(T, H, E, k, I, seed=T + H)
     x, lg = workloads.f32_from_bf16_bits(xb).astype(np.float64), workloads.f32_from_bf16_bits(lb).astype(np.float64)
-    W = moe.ExpertWeights.from_draws(lambda e: experts[e], E, H, I, fmt)
-    act = "bf16" if fmt == "bf16" else "mxfp8"
+    wfmt = "mxfp4" if fmt == "w4a4" else fmt
+    W = moe.ExpertWeights.from_draws(lambda e: experts[e], E, H, I, wfmt)
+    act = {"bf16": "bf16", "w4a4": "mxfp4"}.get(fmt, "mxfp8")
     ref = moe.moe_block(x, lg, W, k, act, keep_intermediate=True)
     # exactness of every sum on the oracle's values (the construction's claim, checked): the
     # terms of each sum are products of factors on grid steps qa and qb, so they all lie on the
@@ -92,14 +95,15 @@ def case(request):
         if act == "bf16":
             ah = np.stack([inter[r] for r in rows])
         else:
-            ah = np.stack([mx.dequantize(*inter[r], "e4m3") for r in rows])
+            el = "e2m1" if act == "mxfp4" else "e4m3"
+            ah = np.stack([mx.dequantize(*inter[r], el) for r in rows])
         _assert_exact(np.abs(ah) @ np.abs(w2).T, _quantum(ah) * _quantum(w2), "down sums")
         d = ah @ w2.T
         for i, (t, j) in enumerate(rows):
             contrib[t, j] = ref.weights[t, j] * d[i]
     _assert_exact(np.abs(contrib).sum(axis=1), _quantum(contrib), "combine sums")
     assert np.array_equal(contrib.sum(axis=1), ref.y)
-    shape = B.Shape.of(T, H, E, k, I, fmt)
+    shape = B.Shape.of(T, H, E, k, I, wfmt, act_fmt=act)
     loader = ExpertLoader(shape, DEV)
     for e in range(E + 1):
         loader.add_expert(e, *experts[e])
@@ -121,8 +125,8 @@ def _ids(o):
 def test_exact_output_and_intermediate(case, opt):
     c = case
     if opt == "one_launch":
-        if c["fmt"] == "bf16" or c["T"] > 128:
-            pytest.skip("the one-launch path takes MX weights and up to 128 tokens")
+        if c["fmt"] in ("bf16", "w4a4") or c["T"] > 128:
+            pytest.skip("the one-launch path takes MX weights, E4M3 activations, up to 128 tokens")
         o = B.Options(0, 0, 0, 0, None, 1)
     else:
         o = None if opt is None else B.Options(opt[0], opt[1], opt[2], 0)
@@ -160,15 +164,22 @@ def test_exact_output_and_intermediate(case, opt):
     hs, _ = _view(ws, c["shape"], o, B.VIEW_HS, torch.uint8)
     h = h.reshape(len(sids), -1)
     hs = hs.reshape(len(sids), -1)
+    a4 = c["fmt"] == "w4a4"
     n = 0
     for r in range(npp):
         f = int(sids[r])
         if f >= S:
             continue
         codes, scales = inter[(f // k1, f % k1)]
-        # +0 and -0 codes (0x00, 0x80) are the same value
-        g = np.where(h[r, :I] == 0x80, 0, h[r, :I])
-        w = np.where(codes == 0x80, 0, codes)
+        if a4:  # E2M1: two codes per byte, element 2i in the low nibble
+            hb = h[r, :I // 2]
+            g = np.stack([hb & 0xF, hb >> 4], axis=-1).reshape(-1)
+            neg0 = 0x8
+        else:
+            g, neg0 = h[r, :I], 0x80
+        # +0 and -0 codes are the same value
+        g = np.where(g == neg0, 0, g)
+        w = np.where(codes == neg0, 0, codes)
         assert np.array_equal(g, w), ("codes", r, f)
         assert np.array_equal(hs[r, :I // 32], scales), ("scales", r, f)
         n += 1

@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_bf16", "decode_mxfp8", "decode_mxfp4", "wide512_mxfp4_T1", "wide512_mxfp4_T6"]
 LARGE = ["prefill_mxfp8", "wide512_mxfp4_T4096"]
 ALL = SMALL + LARGE
+# MXFP4 weights with MXFP4 activations (both MFMA operands E2M1); routing and layout are those of
+# the MXFP8-activation workloads of the same shapes, so only the forward is parametrised over them
+W4A4 = ["decode_w4a4", "wide512_w4a4_T4096"]
 
 
 def _say(*a):
@@ -304,14 +307,14 @@ def _check_forward(name, options):
     return st
 
 
-@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("name", ALL + W4A4)
 def test_forward_parity_default(name):
     _say("forward", name)
     _check_forward(name, None)
 
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "decode_mxfp8", "decode_mxfp4", "wide512_mxfp4_T6",
-                                  "prefill_mxfp8", "wide512_mxfp4_T4096"])
+                                  "prefill_mxfp8", "wide512_mxfp4_T4096"] + W4A4)
 @pytest.mark.parametrize("launcher,combine", [(1, 2), (2, 1), (2, 2), (1, 1)])
 def test_forward_parity_launchers(name, launcher, combine):
     _say("forward", name, launcher, combine)
@@ -319,16 +322,20 @@ def test_forward_parity_launchers(name, launcher, combine):
 
 
 def _check_act_codes(shape, ws, options, xbits):
-    """The activation codes and scales forward left in its workspace against the oracle's MX rule."""
+    """The activation codes and scales forward left in its workspace against the oracle's MX rule
+    (E2M1 codes two per byte, element 2i in the low nibble)."""
     T, H = xbits.shape
     xq, _ = _view(ws, shape, options, B.VIEW_XQ, torch.uint8)
     xs, _ = _view(ws, shape, options, B.VIEW_XS, torch.uint8)
-    rc, rs = mx.quantize(f64(xbits), "e4m3")
-    assert np.array_equal(xq.reshape(T, H), rc)
+    a4 = shape.act_fmt == B.MXMOE_MXFP4_E2M1
+    rc, rs = mx.quantize(f64(xbits), "e2m1" if a4 else "e4m3")
+    if a4:
+        rc = _pack_fp4(rc)
+    assert np.array_equal(xq.reshape(T, -1), rc)
     assert np.array_equal(xs.reshape(T, -1)[:, :H // 32], rs)
 
 
-@pytest.mark.parametrize("name", ["decode_mxfp8", "wide512_mxfp4_T6", "prefill_mxfp8"])
+@pytest.mark.parametrize("name", ["decode_mxfp8", "wide512_mxfp4_T6", "prefill_mxfp8"] + W4A4)
 def test_forward_activation_codes_bit_exact(name):
     # the in-forward quantiser (one-launch and split prologues) against the oracle, every code
     _say("activation codes", name)
@@ -428,7 +435,7 @@ def test_forward_graph_replay(name):
         assert torch.equal(ys.view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["prefill_mxfp8", "wide512_mxfp4_T4096"])
+@pytest.mark.parametrize("name", ["prefill_mxfp8", "wide512_mxfp4_T4096", "wide512_w4a4_T4096"])
 def test_forward_unit_order_invariant(name):
     # The large-M launcher's unit order (runs of units per XCD turn; -1 = one contiguous range per
     # XCD, 1 = linear, 5 = runs that do not divide the unit count) only changes which workgroup

@@ -47,7 +47,7 @@ class Workload:
     top_k: int       # routed experts per token
     I: int           # per-GPU expert intermediate size (N/2 of gate_up, K of down)
     w_fmt: str       # "bf16" | "mxfp8" | "mxfp4"
-    act_fmt: str     # "bf16" | "mxfp8"
+    act_fmt: str     # "bf16" | "mxfp8" | "mxfp4" (MXFP4 with MXFP4 weights only)
     zipf: bool       # add the Zipf(1.1) popularity bias to the router logits
     seed: int = 0
     description: str = ""
@@ -60,10 +60,11 @@ class Workload:
         return replace(self, T=T, name=f"{self.name.rsplit('_T', 1)[0]}_T{T}")
 
 
-def _wide(T: int) -> Workload:
-    return Workload(f"wide512_mxfp4_T{T}", T, 2048, 512, 8, 512, "mxfp4", "mxfp8", True,
+def _wide(T: int, act: str = "mxfp8") -> Workload:
+    tag = "mxfp4" if act == "mxfp8" else "w4a4"
+    return Workload(f"wide512_{tag}_T{T}", T, 2048, 512, 8, 512, "mxfp4", act, True,
                     description="512 routed experts top-8 + shared, hidden 2048, intermediate 512, "
-                                "MXFP4 weights, MXFP8 activations, Zipf(1.1) routing")
+                                f"MXFP4 weights, {act.upper()} activations, Zipf(1.1) routing")
 
 
 WORKLOADS = {
@@ -77,6 +78,10 @@ WORKLOADS = {
         Workload("decode_mxfp4", 128, 3072, 128, 8, 768, "mxfp4", "mxfp8", False,
                  description="decode batch 128, TP2 share (I=768), MXFP4 weights, MXFP8 activations"),
         _wide(1), _wide(6), _wide(4096),
+        # W4A4: both MFMA operands E2M1 (the activations and the intermediate quantised to MXFP4)
+        Workload("decode_w4a4", 128, 3072, 128, 8, 768, "mxfp4", "mxfp4", False,
+                 description="decode batch 128, TP2 share (I=768), MXFP4 weights and activations"),
+        _wide(4096, "mxfp4"),
     ]
 }
 
