@@ -326,7 +326,7 @@ __device__ __forceinline__ void wait_loads_barrier() {
 template <int WF, int LDS_BYTES>
 __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const v4f (&acc)[8][4],
                                                       int r0, int chunk, int wave, int n, int g,
-                                                      int tid, uint8_t* lds) {
+                                                      int tid, uint8_t* lds, int mtv) {
   constexpr bool A4 = a_is_fp4(WF);
   constexpr int kRowBytes = A4 ? 64 : 128;   // code bytes of a row of the tile
   constexpr int kPitch = kRowBytes + 16;     // code row pitch in LDS
@@ -335,6 +335,7 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
   uint32_t* scales = (uint32_t*)(lds + kTileM * kPitch);  // [128] dwords, byte = wave
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
+    if (mt >= mtv) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * mt + 4 * g + i;
@@ -363,10 +364,11 @@ __device__ __forceinline__ void epilogue_gate_up_tile(const GemmParams& p, const
 #pragma unroll
   for (int j = 0; j < kTileM * kUnits / 256; ++j) {
     const int c = tid + 256 * j, row = c / kUnits, unit = c % kUnits;
-    *(v4i*)(p.h + (size_t)(r0 + row) * p.h_stride + kRowBytes * chunk + 16 * unit) =
-        *(const v4i*)(codes + row * kPitch + 16 * unit);
+    if (row < 16 * mtv)
+      *(v4i*)(p.h + (size_t)(r0 + row) * p.h_stride + kRowBytes * chunk + 16 * unit) =
+          *(const v4i*)(codes + row * kPitch + 16 * unit);
   }
-  if (tid < kTileM)
+  if (tid < 16 * mtv)
     *(uint32_t*)(p.hs + (size_t)(r0 + tid) * p.h_srs + 4 * chunk) = scales[tid];
 }
 
@@ -386,7 +388,7 @@ template <int LDS_BYTES>
 __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4f (&acc)[8][4],
                                                    int r0, int chunk, int wave, int n, int g,
                                                    int tid, uint8_t* lds, const int* row_sid,
-                                                   const float* row_w) {
+                                                   const float* row_w, int mtv) {
   constexpr int kPitch = 512 + 32;
   constexpr int kNeed = (kTileM * kPitch + LDS_BYTES - 1) / LDS_BYTES;
   constexpr int kPasses = kNeed <= 1 ? 1 : (kNeed <= 2 ? 2 : (kNeed <= 4 ? 4 : 8));
@@ -401,6 +403,7 @@ __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4
 #pragma unroll
     for (int q = 0; q < kGroups; ++q) {
       const int mt = pass * kGroups + q;
+      if (mt >= mtv) break;  // padding rows only: not stored below
       const v4f wt = *(const v4f*)(row_w + 16 * mt + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -420,6 +423,14 @@ __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4
             *(const v4i*)(lds + lrow * kPitch + 16 * unit);
     }
   }
+}
+
+// Slots (rows with slot id < S) among the 128 rows of a tile; they precede the tile's padding.
+// Every lane of the wave takes part; the count is returned to all of them.
+__device__ __forceinline__ int tile_slots(const int32_t* rows, int S, int lane) {
+  const uint64_t lo = __builtin_amdgcn_ballot_w64(rows[lane] < S);
+  const uint64_t hi = __builtin_amdgcn_ballot_w64(rows[64 + lane] < S);
+  return __builtin_popcountll(lo) + __builtin_popcountll(hi);
 }
 
 // LDS stage of the large-M launcher: the 128 x 128-byte activation tile and its scale dwords
@@ -457,6 +468,14 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   // n_blocks counts 128-row tiles; a layout block of 256 rows (sub_shift 1) holds two of them
   const int r0 = blk * kTileM;
   if (r0 >= *p.num_post_pad) return;
+  // A tile holds rows of one expert, its slots first and then padding. 16-row groups of padding
+  // only (mt >= mtv) skip their MFMAs and their epilogue; down skips the same groups, so the
+  // intermediate rows gate_up leaves unwritten there are never used. Under skewed routing many
+  // experts fill a fraction of a tile (4096 tokens x 512 experts: a quarter of the tiles hold
+  // fewer than 16 slots).
+  const int mtv = __builtin_amdgcn_readfirstlane(
+      (tile_slots(p.sorted_ids + r0, p.S, lane) + 15) >> 4);
+  if (mtv == 0) return;  // a padding-only half of a 256-row layout block
   const int e = p.block_expert[blk >> sub_shift];
   const int wchunk = chunk * kTileWaves + wave;
   TileRows<1> tr;
@@ -470,6 +489,7 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   const v4i ra = rsrc_words(p.a, p.a_bytes);
   const v4i ras = rsrc_words(p.as, p.as_bytes);
   auto act_row = [&](int r, uint32_t stride) -> uint32_t {
+    if (r >= r0 + 16 * mtv) return kOutOfRange;
     if (GATE_UP) {
       const int sid = p.sorted_ids[r];
       return sid < p.S ? (uint32_t)(sid / p.k1) * stride : kOutOfRange;
@@ -520,9 +540,11 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
     a8.hi = A4 ? v4i{0, 0, 0, 0} : *(const v4i*)(base + mt * 16 * kAPitch + u1);
     sa = *(const uint32_t*)(st + L::as + 4 * (16 * mt + n));
   };
-  auto compute = [&](int stage, const Stage<WF, 1>& b, int mt0, int mt1) {
+  // MV (compile time): the 16-row groups the loop multiplies, mtv rounded up to 1, 2, 4 or 8.
+  auto compute = [&](int stage, const Stage<WF, 1>& b, int mt0, int mt1, auto MVC) {
+    constexpr int MV = decltype(MVC)::value;
 #pragma unroll
-    for (int mt = mt0; mt < mt1; ++mt) {
+    for (int mt = mt0; mt < (mt1 < MV ? mt1 : MV); ++mt) {
       v8i a8;
       uint32_t sa;
       a_frag(stage, mt, a8, sa);
@@ -544,8 +566,9 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   // PIPE: the next step's weights go out first, so they have a whole step to arrive, and the
   // activation fragments are read one 16-row group ahead of their MFMAs (two register sets).
   // PRIO: the wave's priority is raised while it issues the step's MFMAs.
-  auto step_pipe = [&](auto SLOT, int ks) {
+  auto step_pipe = [&](auto SLOT, int ks, auto MVC) {
     constexpr int s = decltype(SLOT)::value;
+    constexpr int MV = decltype(MVC)::value;
     const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
     TileRows<1> tn = tr;
     if (oob) tn.w = raw_rsrc(p.w, 0);
@@ -559,47 +582,62 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
       constexpr int mt = decltype(MTI)::value;
       if constexpr (mt + 1 < MT) a_frag(s, mt + 1, a8[(mt + 1) & 1], sa[(mt + 1) & 1]);
       if constexpr (mt == 1) issue_a(1 - s, ks + 1, oob);
-      mma_frags<WF>(a8[mt & 1], (int)(sa[mt & 1] >> (8 * g)), bs[s].b, (int)bs[s].sb, acc[mt]);
+      if constexpr (mt < MV)
+        mma_frags<WF>(a8[mt & 1], (int)(sa[mt & 1] >> (8 * g)), bs[s].b, (int)bs[s].sb, acc[mt]);
       __builtin_amdgcn_sched_barrier(0);
     });
     if (PRIO) __builtin_amdgcn_s_setprio(0);
     wait_loads_barrier<0>();
   };
-  auto step = [&](auto SLOT, int ks) {
+  auto step = [&](auto SLOT, int ks, auto MVC) {
     if constexpr (PIPE) {
-      step_pipe(SLOT, ks);
+      step_pipe(SLOT, ks, MVC);
       return;
     }
     constexpr int s = decltype(SLOT)::value;
     const uint32_t oob = ks + 1 < nks ? 0u : kOutOfRange;
-    compute(s, bs[s], 0, 2);
+    compute(s, bs[s], 0, 2, MVC);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(1 - s, ks + 1, oob);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s, bs[s], 2, 4);
+    compute(s, bs[s], 2, 4, MVC);
     __builtin_amdgcn_sched_barrier(0);
     TileRows<1> tn = tr;
     if (oob) tn.w = raw_rsrc(p.w, 0);
     load_b<WF, 1, 1>(p, tn, ks + 1 < nks ? ks + 1 : 0, lane, bs[1 - s]);
     __builtin_amdgcn_sched_barrier(0);
-    compute(s, bs[s], 4, MT);
+    compute(s, bs[s], 4, MT, MVC);
     __builtin_amdgcn_sched_barrier(0);
     wait_loads_barrier<0>();
   };
-  int ks = 0;
-  for (; ks + 1 < nks; ks += 2) {
-    step(std::integral_constant<int, 0>{}, ks);
-    step(std::integral_constant<int, 1>{}, ks + 1);
-  }
-  if (ks < nks) {  // odd step count: the last step alone (nothing to load)
-    compute(0, bs[0], 0, MT);
-    lds_barrier();  // every wave's reads of stage 0 are done before the epilogue reuses it
+  auto k_loop = [&](auto MVC) {
+    int ks = 0;
+    for (; ks + 1 < nks; ks += 2) {
+      step(std::integral_constant<int, 0>{}, ks, MVC);
+      step(std::integral_constant<int, 1>{}, ks + 1, MVC);
+    }
+    if (ks < nks) {  // odd step count: the last step alone (nothing to load)
+      compute(0, bs[0], 0, MT, MVC);
+      lds_barrier();  // every wave's reads of stage 0 are done before the epilogue reuses it
+    }
+  };
+  // One copy of the loop per group count, so that every loop's MFMAs are unconditional. With
+  // E4M3 activations the kernel is at the register limit, and more than two copies spill.
+  if constexpr (a_is_fp4(WF) || WF == WF_FP4) {
+    if (mtv > 4) k_loop(std::integral_constant<int, 8>{});
+    else if (mtv > 2) k_loop(std::integral_constant<int, 4>{});
+    else if (mtv > 1) k_loop(std::integral_constant<int, 2>{});
+    else k_loop(std::integral_constant<int, 1>{});
+  } else {
+    if (mtv > 2) k_loop(std::integral_constant<int, 8>{});
+    else k_loop(std::integral_constant<int, 2>{});
   }
   if constexpr (GATE_UP) {
-    epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds);
+    epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds, mtv);
   } else {
     if (p.combine == 3)
-      epilogue_down_tile<sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds, row_sid, row_w);
+      epilogue_down_tile<sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds, row_sid, row_w,
+                                      mtv);
     else epilogue_down<MT>(p, acc, r0, r0 + kTileM, wchunk, n, g);
   }
 }
