@@ -473,8 +473,12 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
   // intermediate rows gate_up leaves unwritten there are never used. Under skewed routing many
   // experts fill a fraction of a tile (4096 tokens x 512 experts: a quarter of the tiles hold
   // fewer than 16 slots).
-  const int mtv = __builtin_amdgcn_readfirstlane(
-      (tile_slots(p.sorted_ids + r0, p.S, lane) + 15) >> 4);
+  // Not in the fp8 down pass (three or four K-steps at these shapes): there the count's load at
+  // the start of every tile cost more than the skipped MFMAs saved (8K-token down 210 -> 216 us).
+  constexpr bool kSkip = GATE_UP || WF != WF_FP8;
+  const int mtv = kSkip ? __builtin_amdgcn_readfirstlane(
+                              (tile_slots(p.sorted_ids + r0, p.S, lane) + 15) >> 4)
+                        : kTileM / 16;
   if (mtv == 0) return;  // a padding-only half of a 256-row layout block
   const int e = p.block_expert[blk >> sub_shift];
   const int wchunk = chunk * kTileWaves + wave;
@@ -628,9 +632,11 @@ void k_gemm_tile(GemmParams p, int n_chunks, int n_blocks, int sub_shift) {
     else if (mtv > 2) k_loop(std::integral_constant<int, 4>{});
     else if (mtv > 1) k_loop(std::integral_constant<int, 2>{});
     else k_loop(std::integral_constant<int, 1>{});
-  } else {
+  } else if constexpr (kSkip) {
     if (mtv > 2) k_loop(std::integral_constant<int, 8>{});
     else k_loop(std::integral_constant<int, 2>{});
+  } else {
+    k_loop(std::integral_constant<int, 8>{});
   }
   if constexpr (GATE_UP) {
     epilogue_gate_up_tile<WF, sizeof(lds)>(p, acc, r0, chunk, wave, n, g, tid, lds, mtv);
