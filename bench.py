@@ -365,6 +365,53 @@ def traffic_record(name, kernel_src):
     return rec.get("bytes_per_launch") if rec.get("gemm_src_sha") == h else None
 
 
+def sweep_launchers(specs, tokens, steps=10, warmup=3):
+    """Forward time of the small-M and the large-M launcher (and the automatic plan) over batch
+    sizes, with cold weights as in `measure`. specs: workload names, each optionally suffixed
+    ':uniform' or ':zipf' to set the routing; the workload's other sizes are kept and T varies.
+    Prints one line per (spec, T) to stderr and returns the rows."""
+    import dataclasses
+    import torch
+    import workloads
+    from mx_quantized_grouped_amd import binding as B
+    rows = []
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).to("cuda").view(torch.bfloat16)
+    for spec in specs:
+        base, _, routing = spec.partition(":")
+        g = GpuWorkload(base)
+        w0 = g.w if not routing else dataclasses.replace(g.w, zipf=routing == "zipf")
+        for T in tokens:
+            w = dataclasses.replace(w0, T=T)
+            shape = B.Shape.of(T, w.H, w.E, w.top_k, w.I, w.w_fmt, act_fmt=w.act_fmt)
+            x, lg = to_dev(workloads.draw_x(w)), to_dev(workloads.draw_logits(w))
+            y = torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda")
+            res = {}
+            for tag, opt in [("small", B.Options(1, 0, 0, 0)), ("large", B.Options(2, 0, 0, 0)),
+                             ("auto", None)]:
+                ws = B.new_workspace(B.mxmoe_workspace_bytes(shape, opt), "cuda")
+                for i in range(warmup):
+                    B.mxmoe_forward(shape, x, lg, g.packed[i % len(g.packed)], y=y, workspace=ws,
+                                    options=opt)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for i in range(steps):
+                    B.mxmoe_forward(shape, x, lg, g.packed[i % len(g.packed)], y=y, workspace=ws,
+                                    options=opt)
+                e1.record()
+                torch.cuda.synchronize()
+                res[tag] = e0.elapsed_time(e1) / steps * 1e3
+                del ws
+            r = {"spec": spec, "T": T, "slots_per_expert": T * (w.top_k + 1) / (w.E + 1),
+                 "small_us": res["small"], "large_us": res["large"], "auto_us": res["auto"]}
+            rows.append(r)
+            log(f"sweep {spec} T={T} S/(E+1)={r['slots_per_expert']:.1f}: small {res['small']:.1f}, "
+                f"large {res['large']:.1f}, auto {res['auto']:.1f} us")
+        del g
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +427,11 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run three device-to-device copies of this many MiB (a plain copy "
                          "kernel of known size, to scale HBM byte counters)")
+    ap.add_argument("--sweep-launchers", default="",
+                    help="instead of the bench line: comma-separated workloads (optionally "
+                         "':uniform' / ':zipf') to time with both launchers over --sweep-tokens")
+    ap.add_argument("--sweep-tokens", default="32,64,128,192,224,256,288,320,352,384,512,768,1024,"
+                                              "1536,2048,4096")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the block runs on one GPU's share of the tensor-parallel "
@@ -392,6 +444,11 @@ def main():
         sys.exit(2)
     from mx_quantized_grouped_amd import binding as B
     B.lib()
+    if args.sweep_launchers:
+        rows = sweep_launchers(args.sweep_launchers.split(","),
+                               [int(v) for v in args.sweep_tokens.split(",")])
+        print(json.dumps({"launcher_sweep": rows}), flush=True)
+        return
     if args.calibrate_copy_mb:
         n = args.calibrate_copy_mb << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

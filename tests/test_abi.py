@@ -208,6 +208,19 @@ def test_options_one_launch(L):
         assert B.mxmoe_workspace_bytes(dec, o) == 0
 
 
+def test_auto_launcher_thresholds(L):
+    # the automatic plan's tile height: 128-row tiles (large-M) from 16 slots per expert, or from
+    # 6 with more than 256 experts; 16-row tiles below
+    def bm(T, E, k=8):
+        return B.mxmoe_workspace_view(B.Shape.of(T, 2048, E, k, 512, "mxfp4"), None,
+                                      B.VIEW_SORTED_IDS)[2]
+    assert bm(229, 128) == 16 and bm(230, 128) == 128      # 9 * 230 = 2070 >= 16 * 129 = 2064
+    assert bm(341, 512) == 16 and bm(342, 512) == 128      # 9 * 342 = 3078 >= 6 * 513 = 3078
+    assert bm(128, 128) == 16 and bm(4096, 512) == 128
+    assert B.mxmoe_workspace_view(B.Shape.of(4096, 2048, 512, 8, 512, "mxfp4"),
+                                  B.Options(1, 0, 0, 0), B.VIEW_SORTED_IDS)[2] == 16
+
+
 def test_options_unit_run(L):
     s = B.Shape.of(8192, 3072, 128, 8, 384, "mxfp8")
     assert B.mxmoe_workspace_bytes(s, B.Options(0, 0, 0, -1)) > 0     # one range per XCD
