@@ -144,6 +144,52 @@ def traffic(src, gate_up, out):
     return rec
 
 
+MFMA_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+            "GRBM_GUI_ACTIVE -d <out> -o run -- python3 bench.py --extra none --no-cpu-baseline "
+            "--steps 10 --warmup 3 --workload {wl}")
+
+
+def mfma_util(src, wls, out):
+    """MFMA busy fraction per kernel from prof_mfma_W runs: SQ_VALU_MFMA_BUSY_CYCLES (per SIMD,
+    summed over all SIMDs) over the launch's SIMD-cycles, GRBM_GUI_ACTIVE (summed over the 8
+    XCDs, so / 8 for the GPU's busy cycles) times 1024 SIMDs (256 CUs x 4)."""
+    md = ["# MFMA utilisation of the large-M GEMMs (rocprofv3 counters)", "",
+          "One counter run per workload (rocpd database, `counters_collection` view, one value per "
+          "dispatch and counter, summed over the counter's instances). Per launch: "
+          "SQ_VALU_MFMA_BUSY_CYCLES (a per-SIMD count, summed over all SIMDs) divided by the "
+          "SIMD-cycles of the launch, i.e. GRBM_GUI_ACTIVE (summed over the 8 XCDs, so divided by 8 "
+          "for the GPU's busy cycles) times 1024 SIMDs (256 CUs x 4). Summarised by "
+          "`profile_summary.py --mfma`.", "", "Commands (repository root on the MI355X box):", "",
+          "```"] + [MFMA_CMD.format(wl=wl) for wl in wls] + ["```", "",
+          "| workload | kernel | launches | MFMA busy (% of SIMD-cycles) |", "|---|---|---|---|"]
+    res = {}
+    for wl in wls:
+        c = sqlite3.connect(database(os.path.join(src, f"prof_mfma_{wl}")))
+        rows = c.execute("select dispatch_id, kernel_name, counter_name, sum(value) from "
+                         "counters_collection group by dispatch_id, counter_name").fetchall()
+        disp = {}
+        for d, name, ctr, val in rows:
+            disp.setdefault(d, [name, {}])[1][ctr] = val
+        per = {}
+        for name, v in disp.values():
+            if not ours(name) or short(name).startswith(LOADTIME):
+                continue
+            if not short(name).startswith(("k_gemm_tile", "k_gemm_direct", "k_gate")):
+                continue
+            busy, act = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0)
+            if act > 0:
+                per.setdefault(short(name), []).append(busy / (act / 8 * 1024))
+        for k in sorted(per, key=lambda k: -np.mean(per[k])):
+            md.append(f"| {wl} | `{k}` | {len(per[k])} | {100 * np.mean(per[k]):.1f} |")
+            res[(wl, k)] = float(np.mean(per[k]))
+    md += ["", "`k_gate` is the router gate in front of the block (bf16 MFMA). For launches of a few tens "
+           "of microseconds (the gate) GRBM_GUI_ACTIVE covers more than the kernel, so their fraction "
+           "reads low. The busy count includes the padding rows each tile multiplies."]
+    with open(os.path.join(out, "mfma_util_prefill.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("src", help="directory with the prof_trace_* / prof_pmc_* run outputs")
@@ -151,6 +197,8 @@ def main(argv=None):
         "decode_mxfp8=k_gemm_stream<0, 1, true, 3, 1, 2>",
         "prefill_mxfp8=k_gemm_tile<0, true, true, true>"],
         help="WORKLOAD=gate_up kernel name, for the counter summary")
+    ap.add_argument("--mfma", nargs="*", default=[],
+                    help="workloads with prof_mfma_W counter runs, for mfma_util_prefill.md")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
     for d in sorted(glob.glob(os.path.join(a.src, "prof_trace_*"))):
@@ -160,6 +208,9 @@ def main(argv=None):
             print(wl, {k: round(float(np.mean(v["dur"])), 2) for k, v in t.items()})
     if a.traffic:
         print(json.dumps(traffic(a.src, dict(x.split("=", 1) for x in a.traffic), a.out), indent=1))
+    if a.mfma:
+        for (wl, k), v in mfma_util(a.src, a.mfma, a.out).items():
+            print(wl, k, round(100 * v, 1))
 
 
 if __name__ == "__main__":
