@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
                                                               int cap, AlignOut o) {
   __shared__ int cnt[kAlignMaxE1];
   __shared__ int off[kAlignMaxE1 + 1];
-  __shared__ int s_wave[kAlignWaves];
+  __shared__ int s_wave[2 * kAlignWaves];
   __shared__ int seg_sum[kAlignThreads];
   __shared__ int hist_l[kScanLdsCounts];
   const int t = threadIdx.x;

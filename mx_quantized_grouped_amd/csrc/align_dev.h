@@ -34,7 +34,7 @@ struct AlignSmem {
     uint16_t wcnt[kAlignWaves][kAlignMaxE1];
     unsigned long long bits[kAlignBitmapWords];
   };
-  int s_wave[kAlignWaves];
+  int s_wave[2 * kAlignWaves];
   int16_t tile_e[kTileMapMax];
 };
 
@@ -84,6 +84,33 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_wave, int* total) {
   return before + x - v;
 }
 
+// Exclusive scans of two values at once over the 1024-thread workgroup (one barrier for both):
+// ea / eb the exclusive prefixes, ta / tb the totals. s_wave holds 2 * kAlignWaves ints; the caller
+// puts a barrier between this scan and the next use of s_wave.
+__device__ __forceinline__ void block_excl_scan2(int a, int b, int* s_wave, int* ea, int* eb,
+                                                 int* ta, int* tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
+  if (lane == 63) {
+    s_wave[wave] = xa;
+    s_wave[kAlignWaves + wave] = xb;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < kAlignWaves; ++i) {
+    const int va = s_wave[i], vb = s_wave[kAlignWaves + i];
+    ba += i < wave ? va : 0;
+    bb += i < wave ? vb : 0;
+    sa += va;
+    sb += vb;
+  }
+  *ea = ba + xa - a;
+  *eb = bb + xb - b;
+  *ta = sa;
+  *tb = sb;
+}
+
 __device__ __forceinline__ int align_expert_of(const int32_t* ids, int f, int S, int E1) {
   if (f >= S) return -1;
   int e = ids[f];
@@ -95,19 +122,31 @@ __device__ __forceinline__ int align_expert_of(const int32_t* ids, int f, int S,
 // tile_e: LDS room for kTileMapMax tile -> expert entries, or null. With fill false, the padding
 // slots and the tile -> expert map are left to the caller (the multi-workgroup sort writes them
 // from its parallel passes).
+// align_layout_core takes this thread's two counts (experts 2t and 2t + 1) in registers; cnt (in
+// LDS, all E1 counts) is read only by the padding fill, after the barriers inside. On return off is
+// complete and visible to the workgroup.
+inline __device__ void align_layout_core(int c0, int c1, const int* cnt, int* off, int E1, int S,
+                                         int bm, int cap, int* s_wave, const AlignOut& o,
+                                         int16_t* tile_e, bool fill);
+
 inline __device__ void align_layout_from_counts(const int* cnt, int* off, int E1, int S, int bm,
                                                 int cap, int* s_wave, const AlignOut& o,
                                                 int16_t* tile_e, bool fill = true) {
+  const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+  align_layout_core(e0 < E1 ? cnt[e0] : 0, e1 < E1 ? cnt[e1] : 0, cnt, off, E1, S, bm, cap,
+                    s_wave, o, tile_e, fill);
+}
+
+inline __device__ void align_layout_core(int c0, int c1, const int* cnt, int* off, int E1, int S,
+                                         int bm, int cap, int* s_wave, const AlignOut& o,
+                                         int16_t* tile_e, bool fill) {
   const int t = threadIdx.x;
   const int e0 = 2 * t, e1 = 2 * t + 1;
-  int c0 = e0 < E1 ? cnt[e0] : 0, c1 = e1 < E1 ? cnt[e1] : 0;
   int p0 = (c0 + bm - 1) / bm * bm, p1 = (c1 + bm - 1) / bm * bm;
-  int total;
-  int ex = block_excl_scan(p0 + p1, s_wave, &total);
+  int ex, tx, total, ntouch;
+  block_excl_scan2(p0 + p1, (c0 > 0) + (c1 > 0), s_wave, &ex, &tx, &total, &ntouch);
   if (e0 < E1) off[e0] = ex;
   if (e1 < E1) off[e1] = ex + p0;
-  int ntouch;
-  int tx = block_excl_scan((c0 > 0) + (c1 > 0), s_wave, &ntouch);
   if (o.touched) {
     if (c0 > 0) o.touched[tx] = e0;
     if (c1 > 0) o.touched[tx + (c0 > 0)] = e1;
@@ -192,14 +231,18 @@ inline __device__ void align_small_body(const int32_t* ids, int S, int E1, int b
       if (e >= 0) atomicOr(&sm.bits[e * words + (f >> 6)], 1ull << (f & 63));
     }
     __syncthreads();
-    for (int e = t; e < E1; e += kAlignThreads) {
-      int c = 0;
-      for (int w = 0; w < words; ++w) c += __popcll(sm.bits[e * words + w]);
-      sm.cnt[e] = c;
+    // this thread's two experts (2t, 2t + 1) are counted straight into the layout's scan
+    int c[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * t + h;
+      if (e >= E1) continue;
+      for (int w = 0; w < words; ++w) c[h] += __popcll(sm.bits[e * words + w]);
+      sm.cnt[e] = c[h];
     }
-    __syncthreads();
-    align_layout_from_counts(sm.cnt, sm.off, E1, S, bm, cap, sm.s_wave, o, sm.tile_e);
-    __syncthreads();
+    align_layout_core(c[0], c[1], sm.cnt, sm.off, E1, S, bm, cap, sm.s_wave, o, sm.tile_e, true);
+    // off is complete (the layout's barriers); the scatter writes only valid-slot rows, which the
+    // padding fill above never touches, so no barrier is needed between them
     for (int f = t; f < S; f += kAlignThreads) {
       int e = align_expert_of(ids, f, S, E1);
       if (e < 0) continue;

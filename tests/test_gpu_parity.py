@@ -463,11 +463,13 @@ def test_forward_unit_order_invariant(name):
     (300, 256, 8, 2, 64, "mxfp8"),    # large-M launcher on a small problem
     (300, 256, 8, 2, 128, "bf16"),    # bf16 weights past the launcher threshold: AUTO runs the
                                       # one-wave large-M kernel with bf16 slot rows
+    (5, 256, 4, 4, 96, "w4a4"),       # E2M1 intermediate with a padded K of down
+    (300, 256, 8, 2, 64, "w4a4"),     # W4A4 on the one-wave large-M kernel (I / 32 = 2 chunks)
 ])
 def test_forward_edge_shapes(T, H, E, k, I, fmt):
     _say("edge", T, H, E, k, I, fmt)
-    wl = workloads.Workload(f"edge_{T}_{H}_{E}_{k}_{I}_{fmt}", T, H, E, k, I, fmt,
-                            "bf16" if fmt == "bf16" else "mxfp8", False, 3)
+    w_fmt, act = {"bf16": ("bf16", "bf16"), "w4a4": ("mxfp4", "mxfp4")}.get(fmt, (fmt, "mxfp8"))
+    wl = workloads.Workload(f"edge_{T}_{H}_{E}_{k}_{I}_{fmt}", T, H, E, k, I, w_fmt, act, False, 3)
     from mx_quantized_grouped_amd.weights import ExpertLoader
     shape = shape_of(wl)
     loader = ExpertLoader(shape, DEV)
