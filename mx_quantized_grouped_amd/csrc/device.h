@@ -44,11 +44,15 @@ __device__ __forceinline__ int floor_log2(float a) {
 }
 
 // Shared exponent of an MX block: floor(log2(amax)) - emax_elem, clamped to [-127, 127];
-// an all-zero block gets -127 (scale byte 0).
+// an all-zero block gets -127 (scale byte 0). amax is a block maximum of magnitudes (>= 0,
+// finite). Branch-free: zero takes the subnormal formula, 31 - clz(0) - 149 = -150, which the
+// clamp turns into -127.
 template <int EMAX>
 __device__ __forceinline__ int mx_shared_exp(float amax) {
-  if (!(amax > 0.f)) return -127;
-  int se = floor_log2(amax) - EMAX;
+  const uint32_t u = __float_as_uint(amax);
+  const int e = (int)(u >> 23);
+  const int lg = e ? e - 127 : 31 - (int)__clz(u & 0x7FFFFFu) - 149;
+  const int se = lg - EMAX;
   return se < -127 ? -127 : (se > 127 ? 127 : se);
 }
 

@@ -202,15 +202,20 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), in every lane of the row: the
-// row of an MFMA result fragment, i.e. one 16-column slice of four output rows.
+// Maximum of non-negative finite values over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), in
+// every lane of the row: the row of an MFMA result fragment, i.e. one 16-column slice of four
+// output rows. Non-negative floats order like their bit patterns, so the reduction runs on
+// unsigned integers, one DPP-sourced max per step (a float maximum also canonicalises each
+// operand: two extra instructions per step). Every source lane lies inside the row, so the
+// bound control never applies.
 __device__ __forceinline__ float row16_max(float v) {
+  uint32_t u = __float_as_uint(v);
   // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x128, 0xF, 0xF, false)));
-  return v;
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, true));
+  return __uint_as_float(u);
 }
 
 }  // namespace mxmoe

@@ -77,9 +77,12 @@ __device__ __forceinline__ void quant_act_part(const uint16_t* x, size_t t, int 
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    // quad_perm [1,0,3,2], then [2,3,0,1]: the maximum over the block's four lanes
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0xB1, 0xF, 0xF, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+    // quad_perm [1,0,3,2], then [2,3,0,1]: the maximum over the block's four lanes (non-negative
+    // floats order like their bit patterns; every source lane is inside the quad)
+    uint32_t mu = __float_as_uint(m);
+    mu = max(mu, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mu, 0xB1, 0xF, 0xF, true));
+    mu = max(mu, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mu, 0x4E, 0xF, 0xF, true));
+    m = __uint_as_float(mu);
     if (a4) {
       const int se = mx_shared_exp<2>(m);
       if (part == 0) xs[t * srs + kb] = (uint8_t)(se + 127);
