@@ -77,6 +77,45 @@ def gate_up_flops(w):
 
 
 # ----------------------------------------------------------------------------- GPU leg
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
+STAGE_TIMING = ("mean over the stage-timing pass of a fence-free HIP event pair that the library "
+                "records on its stream around the kernel")
+
+
+class FenceFreeEvents:
+    """n timing events of the HIP runtime already loaded in the process (torch's), created with
+    hipEventDisableSystemFence: recording one skips the system-scope release, which is only
+    needed when the host inspects the memory an event guards, so the interval between two of them
+    is closer to the kernels' own time."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.handles[i] = h.value
+
+    def elapsed_ms(self, i, j):
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), self.handles[i], self.handles[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(h)
+
+
 class GpuWorkload:
     def __init__(self, name, copies=None, threads=16):
         import torch
@@ -186,24 +225,37 @@ class GpuWorkload:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def time_stages(self, steps):
-        """Average duration of each stage, from events the library records on its stream."""
+    def time_stages(self, steps, fence_free=False):
+        """Average duration of each stage, from events the library records on its stream.
+        fence_free: events created with hipEventDisableSystemFence, whose record skips the
+        system-scope release (an L2 write-back and invalidation); a default event pair around a
+        short stage adds ~4 us of that to it."""
         torch, B = self.torch, self.B
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(B.MXMOE_STAGE_EVENTS)]
-               for _ in range(steps)]
-        for row in evs:                  # materialise the underlying hipEvent_t handles
-            for e in row:
-                e.record()
-        torch.cuda.synchronize()
         import ctypes
-        arrs = [(ctypes.c_void_p * B.MXMOE_STAGE_EVENTS)(*[e.cuda_event for e in row]) for row in evs]
+        n = B.MXMOE_STAGE_EVENTS
+        if fence_free:
+            evs = [FenceFreeEvents(n) for _ in range(steps)]
+            arrs = [row.handles for row in evs]
+        else:
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+            for row in evs:              # materialise the underlying hipEvent_t handles
+                for e in row:
+                    e.record()
+            torch.cuda.synchronize()
+            arrs = [(ctypes.c_void_p * n)(*[e.cuda_event for e in row]) for row in evs]
         for i in range(steps):
             opt = B.Options(0, 0, 0, 0, ctypes.cast(arrs[i], ctypes.POINTER(ctypes.c_void_p)))
             self.step(i, opt)
         torch.cuda.synchronize()
         out = {}
         for s, name in enumerate(B.STAGES):
-            out[name] = float(np.mean([row[s].elapsed_time(row[s + 1]) for row in evs]))
+            if fence_free:
+                out[name] = float(np.mean([row.elapsed_ms(s, s + 1) for row in evs]))
+            else:
+                out[name] = float(np.mean([row[s].elapsed_time(row[s + 1]) for row in evs]))
+        if fence_free:
+            for row in evs:
+                row.destroy()
         return out
 
 
@@ -212,7 +264,7 @@ def measure(name, steps, warmup):
     ms, wall_ms = g.time_steps(steps, warmup)
     each = g.time_each(max(10, min(steps, 50)))
     warm_ms = g.time_warm(max(10, min(steps, 50)))
-    stages = g.time_stages(max(10, min(steps, 50)))
+    stages = g.time_stages(max(10, min(steps, 50)), fence_free=True)
     touched = g.touched_experts()
     w = g.w
     by = block_bytes(w, touched)
@@ -239,12 +291,14 @@ def measure(name, steps, warmup):
         ach = gate_up_bytes(w, touched) / (gu_ms * 1e-3) / 1e9
         res["roofline"] = {"kernel": "gate_up", "bound": "hbm", "achieved": ach,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                           "bytes_per_launch": gate_up_bytes(w, touched)}
+                           "bytes_per_launch": gate_up_bytes(w, touched),
+                           "launch_us": gu_ms * 1e3, "timing": STAGE_TIMING}
     else:
         ach = gate_up_flops(w) / (gu_ms * 1e-3) / 1e12
         pk = mfma_peak(w)
         res["roofline"] = {"kernel": "gate_up", "bound": "mfma", "achieved": ach, "peak": pk,
-                           "unit": "TFLOP/s", "frac": ach / pk, "flops_per_launch": gate_up_flops(w)}
+                           "unit": "TFLOP/s", "frac": ach / pk, "flops_per_launch": gate_up_flops(w),
+                           "launch_us": gu_ms * 1e3, "timing": STAGE_TIMING}
     log(f"{name}: {ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
         f"{res['TFLOPs']:.1f} TFLOP/s ({100 * res['mfma_frac']:.1f}% MFMA), stages(us) "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items())
