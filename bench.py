@@ -406,17 +406,27 @@ def cpu_baseline(g, n_tokens, min_seconds=10.0):
             "parity_vs_gpu_on_sample": par}
 
 
-def traffic_record(name, kernel_src):
+GEMM_SOURCES = ("gemm.hip", "gemm_dev.h", "device.h")   # the sources the GEMM kernels compile from
+
+
+def gemm_source_hash():
+    """sha256 (16 hex digits) over the GEMM kernels' sources, in a fixed order."""
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(name):
     """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (else null)."""
+    the current kernel sources (else null)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(name)
     if not rec:
         return None
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    return rec.get("bytes_per_launch") if rec.get("gemm_src_sha") == h else None
+    return rec.get("bytes_per_launch") if rec.get("gemm_src_sha") == gemm_source_hash() else None
 
 
 def sweep_launchers(specs, tokens, steps=10, warmup=3):
@@ -532,8 +542,7 @@ def main():
         gate_shapes.setdefault((wn.T, wn.H, wn.E), n)
     gate = {n: measure_gate(n) for n in gate_shapes.values()}
     rl = dict(head["roofline"])
-    rl["traffic"] = traffic_record(args.workload,
-                                   os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"))
+    rl["traffic"] = traffic_record(args.workload)
     w = workloads.get(args.workload)
     out = {
         "metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1,

@@ -106,8 +106,10 @@ def pmc(db, counter):
 
 def traffic(src, gate_up, out):
     """gate_up: workload -> name of its gate_up kernel in the trace."""
-    sha = hashlib.sha256(open(os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip"),
-                              "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_dev.h", "device.h"):   # bench.py's GEMM_SOURCES, same order
+        h.update(open(os.path.join(ROOT, "mx_quantized_grouped_amd", "csrc", f), "rb").read())
+    sha = h.hexdigest()[:16]
     rec = {}
     md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
           "Two counter runs per workload, one counter each (FETCH_SIZE, then WRITE_SIZE), "

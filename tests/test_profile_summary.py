@@ -57,5 +57,10 @@ def test_trace_and_traffic(tmp_path):
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
     assert rec["read_bytes"] == pytest.approx(1100.0 * 2 * 1024)
     assert rec["write_bytes"] == pytest.approx(6.0 * 1024)
-    gemm = os.path.join(ps.ROOT, "mx_quantized_grouped_amd", "csrc", "gemm.hip")
-    assert rec["gemm_src_sha"] == hashlib.sha256(open(gemm, "rb").read()).hexdigest()[:16]
+    # keyed by the GEMM kernels' sources, the same hash bench.py checks before it reports traffic
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_dev.h", "device.h"):
+        h.update(open(os.path.join(ps.ROOT, "mx_quantized_grouped_amd", "csrc", f), "rb").read())
+    assert rec["gemm_src_sha"] == h.hexdigest()[:16]
+    import bench
+    assert rec["gemm_src_sha"] == bench.gemm_source_hash()
