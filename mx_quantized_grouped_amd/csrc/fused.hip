@@ -614,11 +614,11 @@ __device__ __forceinline__ void role_down(const FusedArgs& a, const FGrid& gd, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (rsid[i] >= S) continue;
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __float_as_int(rw[i] * acc[0][f][i]), ro,
-              (uint32_t)(((size_t)rsid[i] * a.H + 64 * c + n + 16 * f) * 4), 0, kCoherent);
+        // four adjacent columns per lane (the prepack's W2 row order), one coherent 16-byte store
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4i{__float_as_int(rw[i] * acc[0][0][i]), __float_as_int(rw[i] * acc[0][1][i]),
+                __float_as_int(rw[i] * acc[0][2][i]), __float_as_int(rw[i] * acc[0][3][i])},
+            ro, (uint32_t)(((size_t)rsid[i] * a.H + 64 * c + 4 * n) * 4), 0, kCoherent);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -642,7 +642,7 @@ __device__ __forceinline__ void role_down(const FusedArgs& a, const FGrid& gd, i
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) u.shared[wave][4 * g + i][n + 16 * f] = rw[i] * acc[0][f][i];
+    for (int f = 0; f < 4; ++f) u.shared[wave][4 * g + i][4 * n + f] = rw[i] * acc[0][f][i];
   const bool all_in = wait_at_least(a.ctl + kCtlFin + c * gd.n_tg + tg, ntok * a.top_k,
                                     a.spin_limit, a.ctl + kCtlTimeout);
   // lane l: token t0 + l / 4, columns 16 (l % 4) .. + 16 of this chunk

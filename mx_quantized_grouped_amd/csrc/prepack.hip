@@ -15,7 +15,9 @@
 // fragments one wave multiplies in a K-step are adjacent, so a wave streams its weights as one
 // contiguous range. For W13 the tiles alternate gate and up: tile 2p holds gate rows 16p..16p+15
 // and tile 2p+1 up rows I+16p..I+16p+15, so one wave holds matching gate and up columns for the
-// SwiGLU epilogue.
+// SwiGLU epilogue. For W2 the four tiles of a group interleave their rows: tile 4q + f holds rows
+// 64q + 4n + f (n = 0..15), so the four fragments a wave multiplies give each lane four adjacent
+// output columns, stored as one piece by the down epilogues.
 // Scales: per (expert, group of four tiles q, K-step ks) 64 dwords; byte f of lane l = n + 16g is
 // the scale of row n of tile 4q + f for K-block 4ks + g. One dword load per lane and K-step serves
 // the four fragments a wave multiplies (the MFMA's scale operand selects byte f). K is zero-padded
@@ -28,7 +30,7 @@ namespace mxmoe {
 namespace {
 
 __device__ __forceinline__ int src_row(int nt, int n, bool w13, int I) {
-  if (!w13) return nt * 16 + n;
+  if (!w13) return (nt >> 2) * 64 + 4 * n + (nt & 3);
   int p = nt >> 1;
   return (nt & 1) ? I + p * 16 + n : p * 16 + n;
 }
