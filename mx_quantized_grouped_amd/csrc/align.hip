@@ -1,4 +1,5 @@
 // moe_align kernels (the counting sort itself is described in align_dev.h). Two variants:
+//   tiny (S <= 16): every wave derives the layout in registers and writes its share;
 //   small (S <= 4096): one workgroup does count, scan, padding and scatter;
 //   large: per-chunk counts + in-chunk ranks (which also preset every slot of the layout to the
 //   padding sentinel), a one-workgroup scan of the offsets, then a scatter pass that writes the
@@ -14,6 +15,10 @@ namespace {
 
 __global__ __launch_bounds__(kAlignThreads) void k_align_small(const int32_t* ids, int S, int E1,
                                                                int bm, int cap, AlignOut o) {
+  if (S <= kAlignTinyMaxSlots) {
+    align_tiny(ids, o.topk_w, S, E1, bm, cap, o, threadIdx.x >> 6, kAlignWaves);
+    return;
+  }
   __shared__ AlignSmem sm;
   align_small_body(ids, S, E1, bm, cap, o, sm);
 }

@@ -3,8 +3,9 @@
 // microseconds ("Ling-3.0-flash: Tối ưu hóa độ trễ giải mã lên 54% trên 4 GPU Blackwell",
 // "Hai loại thời gian nhàn rỗi": hundreds of 1.5-6 us kernel nodes at batch 1).
 //   up to 32 tokens (and S <= 4096): one launch; workgroup 0 routes every token (each wave takes
-//     at most two, back to back) into LDS and sorts the slots there, the other workgroups quantise
-//     x (and clear the atomic accumulator when that combine is used).
+//     at most two, back to back) into LDS and sorts the slots there (up to 16 slots, each wave
+//     derives the layout in registers), the other workgroups quantise x (and clear the atomic
+//     accumulator when that combine is used).
 //   more tokens: one launch routes (one wave per token, 16 per workgroup) and quantises, then the
 //     sort: one workgroup up to 4096 slots, the three-pass sort beyond.
 #include "align_dev.h"
@@ -24,12 +25,19 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
   if (blockIdx.x == 0) {
     __shared__ AlignSmem sm;
     __shared__ int32_t ids_lds[kAlignSmallMaxSlots];
+    __shared__ float w_lds[kAlignTinyMaxSlots];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int S = a.T * (a.top_k + 1);
+    const bool tiny = S <= kAlignTinyMaxSlots;
     for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.zero_cnt[i] = 0;
     route_tokens_any<F32>(a.logits, wave, kThreads / 64, a.T, a.E, a.top_k, lane, a.ids, a.w,
-                          ids_lds);
+                          ids_lds, tiny ? w_lds : nullptr);
     __syncthreads();
-    align_small_body(ids_lds, a.T * (a.top_k + 1), a.E + 1, a.block_m, a.cap, a.out, sm);
+    if (tiny) {  // every wave derives the few slots' layout and writes its share
+      align_tiny(ids_lds, w_lds, S, a.E + 1, a.block_m, a.cap, a.out, wave, kThreads / 64);
+      return;
+    }
+    align_small_body(ids_lds, S, a.E + 1, a.block_m, a.cap, a.out, sm);
     return;
   }
   const size_t g = (size_t)(blockIdx.x - 1) * kThreads + threadIdx.x;

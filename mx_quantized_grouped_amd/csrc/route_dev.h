@@ -79,10 +79,11 @@ __device__ __forceinline__ void route_load_keys(const void* logits, int t, int E
 }
 
 // Top-k selection, weights and the shared slot for token t from its keys; writes the ids/w rows of
-// width top_k + 1 and, if ids_lds != nullptr, the ids row to LDS too. Called by all 64 lanes.
+// width top_k + 1 and, where ids_lds / w_lds are not null, the same rows to LDS too. Called by all
+// 64 lanes.
 template <bool F32, int NPER>
 __device__ void route_select(uint32_t (&vkey)[NPER], int t, int E, int top_k, int lane,
-                             int32_t* ids, float* w, int32_t* ids_lds) {
+                             int32_t* ids, float* w, int32_t* ids_lds, float* w_lds) {
   uint32_t mine_v = 0, mine_e = 0;  // lane j keeps the j-th selection
   for (int j = 0; j < top_k; ++j) {
     uint32_t lbest = 0;
@@ -129,6 +130,7 @@ __device__ void route_select(uint32_t (&vkey)[NPER], int t, int E, int top_k, in
     ids[(size_t)t * k1 + lane] = id;
     w[(size_t)t * k1 + lane] = wt;
     if (ids_lds) ids_lds[t * k1 + lane] = id;
+    if (w_lds) w_lds[t * k1 + lane] = wt;
   }
 }
 
@@ -136,7 +138,7 @@ __device__ void route_select(uint32_t (&vkey)[NPER], int t, int E, int top_k, in
 // before any is selected, so their load latencies overlap instead of adding up.
 template <bool F32, int NPER>
 __device__ void route_tokens(const void* logits, int t0, int stride, int T, int E, int top_k,
-                             int lane, int32_t* ids, float* w, int32_t* ids_lds) {
+                             int lane, int32_t* ids, float* w, int32_t* ids_lds, float* w_lds) {
   constexpr int B = NPER <= 2 ? 8 : (NPER <= 4 ? 4 : (NPER <= 8 ? 2 : 1));  // <= 16 key registers
   for (int tb = t0; tb < T; tb += B * stride) {
     uint32_t keys[B][NPER];
@@ -148,7 +150,7 @@ __device__ void route_tokens(const void* logits, int t0, int stride, int T, int 
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int t = tb + b * stride;
-      if (t < T) route_select<F32, NPER>(keys[b], t, E, top_k, lane, ids, w, ids_lds);
+      if (t < T) route_select<F32, NPER>(keys[b], t, E, top_k, lane, ids, w, ids_lds, w_lds);
     }
   }
 }
@@ -157,12 +159,13 @@ __device__ void route_tokens(const void* logits, int t0, int stride, int T, int 
 template <bool F32>
 __device__ __forceinline__ void route_tokens_any(const void* logits, int t0, int stride, int T,
                                                  int E, int top_k, int lane, int32_t* ids,
-                                                 float* w, int32_t* ids_lds) {
-  if (E <= 64) route_tokens<F32, 1>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds);
-  else if (E <= 128) route_tokens<F32, 2>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds);
-  else if (E <= 256) route_tokens<F32, 4>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds);
-  else if (E <= 512) route_tokens<F32, 8>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds);
-  else route_tokens<F32, 16>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds);
+                                                 float* w, int32_t* ids_lds,
+                                                 float* w_lds = nullptr) {
+  if (E <= 64) route_tokens<F32, 1>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds, w_lds);
+  else if (E <= 128) route_tokens<F32, 2>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds, w_lds);
+  else if (E <= 256) route_tokens<F32, 4>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds, w_lds);
+  else if (E <= 512) route_tokens<F32, 8>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds, w_lds);
+  else route_tokens<F32, 16>(logits, t0, stride, T, E, top_k, lane, ids, w, ids_lds, w_lds);
 }
 
 }  // namespace mxmoe

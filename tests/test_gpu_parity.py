@@ -238,8 +238,12 @@ def test_align_bit_exact(name, bm):
 def test_align_random_shapes():
     _say("align random shapes")
     rng = np.random.default_rng(9)
-    for T, E, k, bm in [(1, 1, 1, 16), (3, 2, 1, 32), (500, 7, 3, 16), (455, 9, 8, 256),
-                        (5000, 3, 2, 128), (129, 1024, 8, 16), (2000, 1024, 8, 64)]:
+    # up to 16 slots every wave derives the layout in registers (the first five shapes), up to
+    # 4096 slots a workgroup sorts, beyond that the three-pass sort
+    for T, E, k, bm in [(1, 1, 1, 16), (3, 2, 1, 32), (1, 1024, 15, 16), (2, 512, 7, 256),
+                        (5, 2, 2, 64), (7, 1024, 8, 16), (32, 1, 1, 16), (500, 7, 3, 16),
+                        (455, 9, 8, 256), (5000, 3, 2, 128), (129, 1024, 8, 16),
+                        (2000, 1024, 8, 64)]:
         lg = rng.standard_normal((T, E))
         rid, _ = moe.route(lg, k)
         L = moe.align(rid, E, bm)
