@@ -2,9 +2,8 @@
 //   tiny (S <= 16): every wave derives the layout in registers and writes its share;
 //   small (S <= 4096): one workgroup does count, scan, padding and scatter;
 //   large: per-chunk counts + in-chunk ranks (which also preset every slot of the layout to the
-//   padding sentinel), a one-workgroup scan of the offsets, then a scatter pass that writes the
-//   valid slots and the tile -> expert map. Only the offsets go through the single workgroup: its
-//   padding and tile fill took 8 of the 14 us of the 8K-token sort.
+//   padding sentinel), then a placing pass in which every chunk's workgroup derives the offsets
+//   from all chunk histograms and writes its valid slots and part of the tile -> expert map.
 #include "align_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -58,25 +57,35 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_count(const int32_t* id
   }
 }
 
-// Pass 2 (one workgroup): totals, padded offsets and layout outputs; start[c * E1 + e] becomes the
-// absolute start of the (chunk c, expert e) piece. Threads split into (expert, segment of chunks)
-// pairs so the chunk histograms are walked in parallel. When the histograms fit (up to 28 Ki
-// counts), they are first copied into LDS with coalesced loads all issued before the first LDS
-// store (a plain copy loop waits for each load before issuing the next: one memory latency per
-// iteration; batches of 8 per thread still took three memory latencies for 4096 tokens over 512
-// experts); walked in global memory, the per-thread chain of loads made this pass take 16 us for
-// an 8K-token batch.
+// Pass 2: one workgroup per chunk again. Each derives, from all the chunk histograms, the expert
+// totals (hence the padded offsets, by the layout's block scan) and its own chunk's prefix per
+// expert (the slots of earlier chunks), then places its slots: sorted_ids[off[e] + pre[e] + rank]
+// = f (and the slot's weight into sorted_w). The workgroups also write the tile -> expert map, tile
+// b belonging to the expert whose padded range [off[e], off[e + 1]) holds row b * bm (a binary
+// search over the offsets in LDS), -1 past the used rows; workgroup 0 writes the layout's other
+// outputs. Deriving the offsets in every workgroup replaces a one-workgroup scan launch between
+// the count and the scatter (8K tokens x 129 experts: 7.1 + 4.6 us for the two).
+// When the histograms fit (up to 28 Ki counts) they are first copied into LDS with coalesced loads
+// all issued before the first LDS store (a plain copy loop waits for each load before issuing the
+// next: one memory latency per iteration); walked in global memory, every thread's chain of loads
+// costs a memory latency per count.
 constexpr int kScanLdsCounts = 28 * 1024;
 
-// The scan proper over the chunk histograms `hist` (LDS or global). It is inlined once per
-// address space: through one pointer that may be either, every read of the walks below became a
-// generic (flat) load waited on one at a time, ~70 of them per thread for 4096 tokens over 512
-// experts.
-__device__ __forceinline__ void align_scan_body(const int32_t* __restrict__ hist,
-                                                int32_t* __restrict__ start,
-                                                int32_t* __restrict__ offs, int nchunks, int S,
-                                                int E1, int bm, int cap, const AlignOut& o,
-                                                int* cnt, int* off, int* s_wave, int* seg_sum) {
+struct PlaceSmem {
+  int cnt[kAlignMaxE1];
+  int pre[kAlignMaxE1];
+  int off[kAlignMaxE1 + 1];
+  int s_wave[2 * kAlignWaves];
+  int seg_all[kAlignThreads];
+  int seg_pre[kAlignThreads];
+};
+
+// Expert totals cnt[e] and this chunk's prefix pre[e] over the chunk histograms `hist` (LDS or
+// global). Threads split into (expert, segment of chunks) pairs so the histograms are walked in
+// parallel. Inlined once per address space: through one pointer that may be either, every read
+// became a generic (flat) load waited on one at a time.
+__device__ __forceinline__ void align_chunk_sums(const int32_t* __restrict__ hist, int nchunks,
+                                                 int chunk, int E1, PlaceSmem& sm) {
   const int t = threadIdx.x;
   const int P = E1 >= kAlignThreads ? 1 : kAlignThreads / E1;  // segments per expert
   const int seg = (nchunks + P - 1) / P;
@@ -90,53 +99,51 @@ __device__ __forceinline__ void align_scan_body(const int32_t* __restrict__ hist
   // experts beyond the first 1024 (E1 > 1024) are summed by a second pass of the same threads
   for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
     if (pass == 1 && (P != 1 || ee >= E1)) break;
-    int sum = 0;
+    int all = 0, before = 0;
     if (mine && ee < E1) {
 #pragma unroll 8
-      for (int c = c_lo; c < c_hi; ++c) sum += hist[(size_t)c * E1 + ee];
+      for (int c = c_lo; c < c_hi; ++c) {
+        const int v = hist[(size_t)c * E1 + ee];
+        all += v;
+        before += c < chunk ? v : 0;
+      }
     }
-    if (pass == 0) seg_sum[t] = sum;
-    else cnt[ee] = sum;
+    if (pass == 0) {
+      sm.seg_all[t] = all;
+      sm.seg_pre[t] = before;
+    } else {
+      sm.cnt[ee] = all;
+      sm.pre[ee] = before;
+    }
   }
   __syncthreads();
   for (int x = t; x < E1 && x < kAlignThreads; x += kAlignThreads) {
-    if (P == 1) { cnt[x] = seg_sum[x]; continue; }
-    int s2 = 0;
+    int a = 0, b = 0;
     for (int q = 0; q < P; ++q) {
-      int v = seg_sum[q * E1 + x];
-      seg_sum[q * E1 + x] = s2;  // exclusive prefix over segments
-      s2 += v;
+      a += sm.seg_all[q * E1 + x];
+      b += sm.seg_pre[q * E1 + x];
     }
-    cnt[x] = s2;
+    sm.cnt[x] = a;
+    sm.pre[x] = b;
   }
   __syncthreads();
-  align_layout_from_counts(cnt, off, E1, S, bm, cap, s_wave, o, nullptr, false);
-  for (int x = t; x <= E1; x += kAlignThreads) offs[x] = off[x];
-  __syncthreads();
-  for (int ee = e, pass = 0; pass < 2; ++pass, ee += kAlignThreads) {
-    if (pass == 1 && (P != 1 || ee >= E1)) break;
-    if (!mine || ee >= E1) continue;
-    int run = off[ee] + (P == 1 ? 0 : seg_sum[t]);
-#pragma unroll 8
-    for (int c = c_lo; c < c_hi; ++c) {
-      start[(size_t)c * E1 + ee] = run;
-      run += hist[(size_t)c * E1 + ee];
-    }
-  }
 }
 
-__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __restrict__ hist_g,
-                                                              int32_t* __restrict__ start,
-                                                              int32_t* __restrict__ offs,
-                                                              int nchunks, int S, int E1, int bm,
-                                                              int cap, AlignOut o) {
-  __shared__ int cnt[kAlignMaxE1];
-  __shared__ int off[kAlignMaxE1 + 1];
-  __shared__ int s_wave[2 * kAlignWaves];
-  __shared__ int seg_sum[kAlignThreads];
+__global__ __launch_bounds__(kAlignThreads) void k_align_place(const int32_t* ids, int S, int E1,
+                                                               int bm, int cap, int nb,
+                                                               const int32_t* rank_in,
+                                                               const int32_t* __restrict__ hist_g,
+                                                               int nchunks, AlignOut o) {
+  __shared__ PlaceSmem sm;
   __shared__ int hist_l[kScanLdsCounts];
-  const int t = threadIdx.x;
+  __shared__ int npp_local;
+  const int t = threadIdx.x, c = blockIdx.x;
   const int nh = nchunks * E1;
+  // this thread's slot: its loads go out first, to arrive while the histograms are summed
+  const int f = c * kAlignThreads + t;
+  const int e = align_expert_of(ids, f, S, E1);
+  const int rank = e >= 0 ? rank_in[f] : 0;
+  const float wt = (e >= 0 && o.sorted_w) ? o.topk_w[f] : 0.f;
   if (nh <= kScanLdsCounts) {
     constexpr int kB = kScanLdsCounts / kAlignThreads;  // every load in one batch
     for (int base = t; base < nh; base += kB * kAlignThreads) {
@@ -153,45 +160,36 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const int32_t* __r
       }
     }
     __syncthreads();
-    align_scan_body(hist_l, start, offs, nchunks, S, E1, bm, cap, o, cnt, off, s_wave, seg_sum);
+    align_chunk_sums(hist_l, nchunks, c, E1, sm);
   } else {
-    align_scan_body(hist_g, start, offs, nchunks, S, E1, bm, cap, o, cnt, off, s_wave, seg_sum);
+    align_chunk_sums(hist_g, nchunks, c, E1, sm);
   }
-}
-
-// Pass 3: sorted_ids[start(chunk, e) + rank] = f (and the slot's weight into sorted_w); the
-// workgroups also write the tile -> expert map, tile b belonging to the expert whose padded range
-// [offs[e], offs[e + 1]) holds row b * bm (a binary search over the offsets in LDS), -1 past the
-// used rows.
-__global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const int32_t* ids, int S, int E1,
-                                                                 int bm, int nb,
-                                                                 const int32_t* rank_in,
-                                                                 const int32_t* start,
-                                                                 const int32_t* offs, AlignOut o) {
-  __shared__ int off[kAlignMaxE1 + 1];
-  const int t = threadIdx.x;
-  const int f = blockIdx.x * kAlignThreads + t;
-  const int e = align_expert_of(ids, f, S, E1);
+  // offsets; only workgroup 0 writes the layout's count, offsets and touched list
+  AlignOut lo = o;
+  if (c != 0) {
+    lo.num_post_pad = &npp_local;
+    lo.expert_off = nullptr;
+    lo.touched = nullptr;
+    lo.n_touched = nullptr;
+  }
+  align_layout_from_counts(sm.cnt, sm.off, E1, S, bm, cap, sm.s_wave, lo, nullptr, false);
   if (e >= 0) {
-    const int pos = start[(size_t)blockIdx.x * E1 + e] + rank_in[f];
+    const int pos = sm.off[e] + sm.pre[e] + rank;
     o.sorted_ids[pos] = f;
-    if (o.sorted_w) o.sorted_w[pos] = o.topk_w[f];
+    if (o.sorted_w) o.sorted_w[pos] = wt;
   }
-  if (blockIdx.x * kAlignThreads >= nb) return;  // workgroup-uniform: no tiles left for it
-  for (int x = t; x <= E1; x += kAlignThreads) off[x] = offs[x];
-  __syncthreads();
-  const int total = off[E1];
-  for (int b = blockIdx.x * kAlignThreads + t; b < nb; b += gridDim.x * kAlignThreads) {
+  const int total = sm.off[E1];
+  for (int b = c * kAlignThreads + t; b < nb; b += gridDim.x * kAlignThreads) {
     const int r = b * bm;
     int be = -1;
     if (r < total) {
-      int lo = 0, hi = E1 - 1;  // largest e with off[e] <= r (empty experts share offsets)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r) lo = mid;
+      int lo2 = 0, hi = E1 - 1;  // largest e with off[e] <= r (empty experts share offsets)
+      while (lo2 < hi) {
+        const int mid = (lo2 + hi + 1) >> 1;
+        if (sm.off[mid] <= r) lo2 = mid;
         else hi = mid - 1;
       }
-      be = lo;
+      be = lo2;
     }
     o.block_expert[b] = be;
   }
@@ -210,8 +208,7 @@ size_t align_scratch_bytes(int T, int E, int top_k) {
   size_t nch = (S + kAlignChunk - 1) / kAlignChunk;
   size_t rank = (S * 4 + 255) / 256 * 256;
   size_t hist = (nch * (size_t)(E + 1) * 4 + 255) / 256 * 256;
-  size_t offs = ((size_t)(E + 2) * 4 + 255) / 256 * 256;
-  return rank + 2 * hist + offs;  // rank, chunk histograms, chunk starts, expert offsets
+  return rank + hist;  // in-chunk ranks, chunk histograms
 }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m,
@@ -225,16 +222,11 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int top_k, int block_m
   }
   const int nch = (S + kAlignChunk - 1) / kAlignChunk;
   int32_t* rank = (int32_t*)scratch;
-  const size_t hist_bytes = ((size_t)nch * E1 * 4 + 255) / 256 * 256;
   int32_t* hist = (int32_t*)((char*)scratch + ((size_t)S * 4 + 255) / 256 * 256);
-  int32_t* start = (int32_t*)((char*)hist + hist_bytes);
-  int32_t* offs = (int32_t*)((char*)start + hist_bytes);
   hipLaunchKernelGGL(k_align_count, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, cap, rank,
                      hist, o);
-  hipLaunchKernelGGL(k_align_scan, dim3(1), dim3(kAlignThreads), 0, st, hist, start, offs, nch, S,
-                     E1, block_m, cap, o);
-  hipLaunchKernelGGL(k_align_scatter, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, block_m,
-                     cap / block_m, rank, start, offs, o);
+  hipLaunchKernelGGL(k_align_place, dim3(nch), dim3(kAlignThreads), 0, st, ids, S, E1, block_m,
+                     cap, cap / block_m, rank, hist, nch, o);
   return hipGetLastError();
 }
 
