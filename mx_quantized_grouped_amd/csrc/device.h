@@ -33,6 +33,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two fp32 values to bf16, round to nearest even, a in the low half: one v_cvt_pk_bf16_f32 on
+// gfx950 (the integer form above takes about four instructions per value plus the packing).
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{a, b}, v2bf_t));
+}
 
 // ---------------------------------------------------------------------------- MX encoding
 // floor(log2(a)) for finite a > 0 (fp32 subnormals included), from the exponent bits.

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void k_finalize(const void* out, int T, int H,
   v4i o;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    o[i] = (int)(f32_to_bf16_bits(s[2 * i]) | (f32_to_bf16_bits(s[2 * i + 1]) << 16));
+    o[i] = (int)bf16_pair(s[2 * i], s[2 * i + 1]);
   *(v4i*)(y + t * H + c) = o;
 }
 

@@ -679,7 +679,7 @@ __device__ __forceinline__ void role_down(const FusedArgs& a, const FGrid& gd, i
     for (int x = 0; x < 8; ++x) {
       const float s0 = acc16[2 * x] + u.shared[wave][tr_][16 * q + 2 * x];
       const float s1 = acc16[2 * x + 1] + u.shared[wave][tr_][16 * q + 2 * x + 1];
-      o[x] = f32_to_bf16_bits(s0) | (f32_to_bf16_bits(s1) << 16);
+      o[x] = bf16_pair(s0, s1);
     }
     uint16_t* yr = a.y + (size_t)t * a.H + col;
     *(v4i*)yr = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};

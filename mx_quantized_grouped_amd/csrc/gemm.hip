@@ -96,8 +96,8 @@ __device__ __forceinline__ void store_down_row(const GemmParams& p, int sid, flo
                                                float v1, float v2, float v3, int c0) {
   if (p.combine == 3) {
     uint2 o;
-    o.x = f32_to_bf16_bits(wt * v0) | (f32_to_bf16_bits(wt * v1) << 16);
-    o.y = f32_to_bf16_bits(wt * v2) | (f32_to_bf16_bits(wt * v3) << 16);
+    o.x = bf16_pair(wt * v0, wt * v1);
+    o.y = bf16_pair(wt * v2, wt * v3);
     *(uint2*)((uint16_t*)p.out32 + (size_t)sid * p.H + c0) = o;
   } else if (p.combine == 1) {
     *(v4f*)(p.out32 + (size_t)sid * p.H + c0) = v4f{wt * v0, wt * v1, wt * v2, wt * v3};
@@ -163,8 +163,8 @@ __device__ __forceinline__ void finalize_chunk_if_last(const GemmParams& p, int 
     for (int c = 0; c < 4; ++c)
       v[c] = __hip_atomic_load(src + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint2 o;
-    o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    o.x = bf16_pair(v[0], v[1]);
+    o.y = bf16_pair(v[2], v[3]);
     *(uint2*)(p.y + (size_t)t * p.H + col) = o;
   }
 }
@@ -494,8 +494,8 @@ __device__ __forceinline__ void epilogue_down_tile(const GemmParams& p, const v4
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint2 o;
-      o.x = f32_to_bf16_bits(wt[i] * acc[mt][0][i]) | (f32_to_bf16_bits(wt[i] * acc[mt][1][i]) << 16);
-      o.y = f32_to_bf16_bits(wt[i] * acc[mt][2][i]) | (f32_to_bf16_bits(wt[i] * acc[mt][3][i]) << 16);
+      o.x = bf16_pair(wt[i] * acc[mt][0][i], wt[i] * acc[mt][1][i]);
+      o.y = bf16_pair(wt[i] * acc[mt][2][i], wt[i] * acc[mt][3][i]);
       if (sd[i] < p.S) *(uint2*)(out16 + (size_t)sd[i] * p.H + 64 * wchunk + 4 * n) = o;
     }
   }
