@@ -517,6 +517,33 @@ def test_forward_wide_tiles(T, H, E, k, I, fmt):
         assert tolerance_ok(st), (opt.combine, st)
 
 
+# Small-M launcher forced on ~380 16-row tiles (past the split-K unit count, so one wave per unit
+# on gate_up and the shared-tile down pass): K-step counts 4, 12 and 8 (at 4 the fp8 ring drops
+# from 3 stages to 2), 4 and 8 column chunks, fp8 / fp4 weights and E2M1 activations
+@pytest.mark.parametrize("T,H,E,k,I,fmt", [
+    (1100, 512, 40, 4, 128, "mxfp8"),
+    (1100, 1536, 40, 4, 128, "mxfp4"),
+    (1100, 1024, 40, 4, 256, "w4a4"),
+])
+def test_forward_small_m_many_tiles(T, H, E, k, I, fmt):
+    _say("small-M many tiles", T, H, E, k, I, fmt)
+    w_fmt, act = {"w4a4": ("mxfp4", "mxfp4")}.get(fmt, (fmt, "mxfp8"))
+    wl = workloads.Workload(f"sa_{T}_{H}_{E}_{k}_{I}_{fmt}", T, H, E, k, I, w_fmt, act, False, 17)
+    from mx_quantized_grouped_amd.weights import ExpertLoader
+    shape = shape_of(wl)
+    loader = ExpertLoader(shape, DEV)
+    for e in range(E + 1):
+        loader.add_expert(e, *workloads.draw_expert(wl, e))
+    packed = loader.finish()
+    xb, lb = workloads.draw_x(wl), workloads.draw_logits(wl)
+    ref = moe.moe_block(f64(xb), f64(lb), oracle_weights(wl), k, wl.act_fmt)
+    for opt in [B.Options(1, 1, 0, 0), B.Options(1, 3, 0, 0)]:
+        y = B.mxmoe_forward(shape, bf16_tensor(xb), bf16_tensor(lb), packed, options=opt)
+        torch.cuda.synchronize()
+        st = moe.parity_stats(y.float().cpu().numpy(), ref.y)
+        assert tolerance_ok(st), (opt.combine, st)
+
+
 # Degenerate routing: equal logits send every token to experts 0 .. k-1 (ties go to the lower
 # index), so two experts and the shared one hold every slot and the rest are untouched: the
 # largest per-expert row counts the layout can have, on both launchers and every combine.
