@@ -104,8 +104,19 @@ typedef struct {
   int32_t spin_limit;
   int32_t hold;     /* tests only: 1 = the one-launch path never publishes its layout, so every
                        wait on it gives up (exercises the bounded waits); 0 otherwise */
-  int32_t reserved; /* must be 0 */
+  /* Row layout of the small-M launcher, MXMOE_LAYOUT_*: AUTO = the library's choice; SORTED = the
+     aligned layout of mxmoe_align (slots sorted by expert, tiles padded to block_m); SLOTS = no
+     sort: every expert owns T rows of the intermediate, the gate_up units find a routed expert's
+     slots themselves by a scan of the routing table (in slot order; the shared expert's are its
+     tokens in order) and record them for the down pass. SLOTS needs the small-M launcher,
+     16-row tiles, a slot-row combine and T <= 256 (MXMOE_EUNSUPPORTED otherwise); AUTO takes it
+     where at least as many slots as experts make most experts' scans find rows and the
+     intermediate of T rows per expert stays within 64 MiB. Each output row is the same sums in
+     the same order in both layouts (bit-identical outputs), except where the sorted plan splits
+     K over four waves (few units: a handful of tokens), which reorders the sums. */
+  int32_t layout;
 } mxmoe_options;
+enum { MXMOE_LAYOUT_AUTO = 0, MXMOE_LAYOUT_SORTED = 1, MXMOE_LAYOUT_SLOTS = 2 };
 #define MXMOE_STAGE_EVENTS 5
 
 /* Host: static description of a status code. Never NULL. */
@@ -232,7 +243,10 @@ int mxmoe_forward_noalloc(const mxmoe_shape* s, const void* x, const void* logit
  * slot sorted_ids[r]; Ip = I rounded up to a multiple of 128; E4M3 codes for MX weights, bf16
  * values for bf16 weights), 9 intermediate scale bytes [cap, srs_I] (K-block order, srs_I = Ip/32
  * rounded up to a multiple of 16; MX weights only). Rows of padding slots and columns past I are
- * unspecified. 10 (MXMOE_VIEW_STATUS) the status word of the last one-launch call on this
+ * unspecified. In the slot-order plan (mxmoe_options.layout) view 2 holds (E+1)*T entries, entry
+ * e*T + i the slot of expert e's i-th row (slot order; T*(top_k+1) past its count), views 3-5
+ * have size 0, and row e*T + i of views 8 and 9 belongs to entry e*T + i of view 2.
+ * 10 (MXMOE_VIEW_STATUS) the status word of the last one-launch call on this
  * workspace (int32: 0 every wait completed, 1 a bounded wait gave up and the output is not valid).
  * Returns the byte offset and writes the byte size to *bytes; the tile height forward used is
  * written to *block_m. Returns (size_t)-1 for an invalid request. */

@@ -18,6 +18,7 @@ MXMOE_OK, MXMOE_EINVAL, MXMOE_EUNSUPPORTED, MXMOE_EWORKSPACE, MXMOE_EHIP = 0, -1
 MXMOE_BF16, MXMOE_F32, MXMOE_MXFP8_E4M3, MXMOE_MXFP4_E2M1 = 0, 1, 2, 3
 MXMOE_LAUNCH_AUTO, MXMOE_LAUNCH_SMALL_M, MXMOE_LAUNCH_LARGE_M = 0, 1, 2
 MXMOE_COMBINE_AUTO, MXMOE_COMBINE_SLOTS, MXMOE_COMBINE_ATOMIC, MXMOE_COMBINE_SLOTS_BF16 = 0, 1, 2, 3
+MXMOE_LAYOUT_AUTO, MXMOE_LAYOUT_SORTED, MXMOE_LAYOUT_SLOTS = 0, 1, 2
 (VIEW_TOPK_IDS, VIEW_TOPK_W, VIEW_SORTED_IDS, VIEW_BLOCK_EXPERT, VIEW_NUM_POST_PAD, VIEW_EXPERT_OFF,
  VIEW_XQ, VIEW_XS, VIEW_H, VIEW_HS, VIEW_STATUS) = range(11)
 WORKSPACE_CONTROL_BYTES = 72 * 1024
@@ -63,7 +64,7 @@ class Options(ctypes.Structure):
                 ("block_m", ctypes.c_int32), ("unit_run", ctypes.c_int32),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("fused", ctypes.c_int32), ("spin_limit", ctypes.c_int32),
-                ("hold", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("hold", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class MxMoeError(RuntimeError):

@@ -1,6 +1,7 @@
 // C ABI of the MX MoE block: argument validation, workspace plan, launcher choice and the launch
 // sequence route -> align -> quant -> gate_up (+SwiGLU, requant) -> down (+weighted combine) ->
 // bf16 output. Everything is enqueued on the caller's stream; nothing is read back to the host.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -27,6 +28,7 @@ Tuning read_tuning() {
   t.stream_depth = env_int("MXMOE_STREAM_DEPTH", -1);
   t.prio = env_int("MXMOE_PRIO", -1);
   t.tile_pipe = env_int("MXMOE_TILE_PIPE", -1);
+  t.slot_order = env_int("MXMOE_SLOT_ORDER", -1);
   t.final_nt = env_int("MXMOE_NT", -1);
   t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
   return t;
@@ -125,6 +127,9 @@ struct Plan {
   int xrow, hrow;  // bytes of an activation-code row [H] and of an intermediate row [Ip]
   int unit_run;  // large-M unit order from the options (0 = the launcher's default)
   bool fused;    // the one-launch path (small batches)
+  bool so;       // slot-order plan: no sort (small-M launcher)
+  int so_tiles;  // its shared-expert tiles of 16 tokens
+  int hrows;     // intermediate rows: the layout's capacity, or T per expert in slot order
   int spin_limit, hold;
   size_t off[NSEG + 1];
 };
@@ -136,8 +141,8 @@ bool within_offsets(const Plan& p) {
   const size_t lim = kMaxBufferBytes;
   if ((size_t)p.T * p.xrow >= lim) return false;
   if ((size_t)p.T * p.srs_H >= lim) return false;
-  if ((size_t)p.cap * p.hrow >= lim) return false;
-  if ((size_t)p.cap * p.srs_I >= lim) return false;
+  if ((size_t)p.hrows * p.hrow >= lim) return false;
+  if ((size_t)p.hrows * p.srs_I >= lim) return false;
   return true;
 }
 
@@ -146,7 +151,8 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   if (rc) return rc;
   mxmoe_options o = opt ? *opt : mxmoe_options{0, 0, 0, 0, nullptr, 0, 0, 0, 0};
   if (o.launcher < 0 || o.launcher > 2 || o.combine < 0 || o.combine > 3 || o.unit_run < -1 ||
-      o.fused < -1 || o.fused > 1 || o.spin_limit < 0 || o.hold < 0 || o.hold > 1 || o.reserved)
+      o.fused < -1 || o.fused > 1 || o.spin_limit < 0 || o.hold < 0 || o.hold > 1 ||
+      o.layout < 0 || o.layout > 2)
     return MXMOE_EINVAL;
   if (o.block_m != 0 && !valid_block_m(o.block_m)) return MXMOE_EINVAL;
   Plan& p = *P;
@@ -176,28 +182,44 @@ int make_plan(const mxmoe_shape* s, const mxmoe_options* opt, Plan* P) {
   p.combine = o.combine ? o.combine : (p.large ? MXMOE_COMBINE_SLOTS_BF16 : MXMOE_COMBINE_SLOTS);
   p.fuse_final = !p.large && p.combine == MXMOE_COMBINE_ATOMIC && p.T <= kFuseFinalMaxT;
   p.bm = o.block_m ? o.block_m : (p.large ? (p.mx ? 128 : 64) : 16);
+  // Slot order (no sort; each small-M unit finds its expert's rows itself) where most experts
+  // have rows and K is not split; requested explicitly, any small-M plan with 16-row tiles, slot
+  // rows and at most kSlotOrderMaxT tokens.
+  const bool so_ok = !p.large && !p.fused && p.combine != MXMOE_COMBINE_ATOMIC && p.bm == 16 &&
+                     p.T <= kSlotOrderMaxT;
+  if (o.layout == MXMOE_LAYOUT_SLOTS && !so_ok) return MXMOE_EUNSUPPORTED;
+  p.so = o.layout == MXMOE_LAYOUT_SLOTS ||
+         (o.layout == MXMOE_LAYOUT_AUTO && so_ok && tuning().slot_order != 0 &&
+          slot_order_fits(p.T, p.E, p.k, p.I));
+  p.so_tiles = (p.T + 15) / 16;
   p.cap = (int)cap_of(p.S, p.E1, p.bm);
   p.Ip = round_up(p.I, KSTEP);
   p.srs_H = scale_row_bytes(p.H);
   p.srs_I = scale_row_bytes(p.Ip);
   p.xrow = !p.mx ? 2 * p.H : (a_is_fp4(p.wf) ? p.H / 2 : p.H);
   p.hrow = !p.mx ? 2 * p.Ip : (a_is_fp4(p.wf) ? p.Ip / 2 : p.Ip);
+  // slot order keeps T intermediate rows per expert (every expert's rows at a fixed place, so the
+  // down pass needs no lookup before its copy); the automatic choice bounds what that costs
+  if (p.so && o.layout == MXMOE_LAYOUT_AUTO &&
+      (size_t)p.E1 * p.T * p.hrow > kSlotOrderMaxRowBytes)
+    p.so = false;
+  p.hrows = p.so ? std::max(p.cap, p.E1 * p.T) : p.cap;
   p.unit_run = o.unit_run;
   if (!within_offsets(p)) return MXMOE_EUNSUPPORTED;
   size_t sz[NSEG];
   sz[SEG_CTL] = kFusedCtlBytes;  // first in every plan, so any call may follow any other
   sz[SEG_IDS] = (size_t)p.S * 4;
   sz[SEG_W] = (size_t)p.S * 4;
-  sz[SEG_SORTED] = (size_t)p.cap * 4;
+  sz[SEG_SORTED] = (size_t)(p.so ? p.E1 * p.T : p.cap) * 4;  // slot order: per-expert slot lists
   sz[SEG_BLOCKEXP] = (size_t)(p.cap / p.bm) * 4;
   sz[SEG_COUNTERS] = 16;
-  sz[SEG_EXPOFF] = (size_t)(p.E1 + 1) * 4;
+  sz[SEG_EXPOFF] = (size_t)(p.E1 + 1) * 4;  // slot order: per-expert row counts
   sz[SEG_TOUCHED] = (size_t)p.E1 * 4;
   sz[SEG_ALIGN] = align_scratch_bytes(p.T, p.E, p.k);
   sz[SEG_XQ] = p.mx ? (size_t)p.T * p.xrow : 0;
   sz[SEG_XS] = p.mx ? (size_t)p.T * p.srs_H : 0;
-  sz[SEG_H] = (size_t)p.cap * p.hrow;
-  sz[SEG_HS] = p.mx ? (size_t)p.cap * p.srs_I : 0;
+  sz[SEG_H] = (size_t)p.hrows * p.hrow;
+  sz[SEG_HS] = p.mx ? (size_t)p.hrows * p.srs_I : 0;
   sz[SEG_DONE] = p.fuse_final ? (size_t)(p.H / 64) * 4 : 0;
   sz[SEG_SORTW] = (size_t)p.cap * 4;
   sz[SEG_OUT] = p.combine == MXMOE_COMBINE_ATOMIC ? (size_t)p.T * p.H * 4
@@ -349,10 +371,11 @@ size_t mxmoe_workspace_view(const mxmoe_shape* s, const mxmoe_options* opt, int 
   static const int segs[MXMOE_VIEW_COUNT] = {SEG_IDS, SEG_W,  SEG_SORTED, SEG_BLOCKEXP, SEG_COUNTERS,
                                              SEG_EXPOFF, SEG_XQ, SEG_XS, SEG_H, SEG_HS, SEG_CTL};
   if (which < 0 || which >= MXMOE_VIEW_COUNT) return (size_t)-1;
+  const bool lay = !p.so;  // slot order: per-expert slot lists in place of the sorted rows
   const size_t sz[MXMOE_VIEW_COUNT] = {
-      (size_t)p.S * 4, (size_t)p.S * 4, (size_t)p.cap * 4, (size_t)(p.cap / p.bm) * 4, 4,
-      (size_t)(p.E1 + 1) * 4, p.mx ? (size_t)p.T * p.xrow : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
-      (size_t)p.cap * p.hrow, p.mx ? (size_t)p.cap * p.srs_I : 0, 4};
+      (size_t)p.S * 4, (size_t)p.S * 4, (size_t)(lay ? p.cap : p.E1 * p.T) * 4,
+      lay ? (size_t)(p.cap / p.bm) * 4 : 0, lay ? 4u : 0u, lay ? (size_t)(p.E1 + 1) * 4 : 0, p.mx ? (size_t)p.T * p.xrow : 0, p.mx ? (size_t)p.T * p.srs_H : 0,
+      (size_t)p.hrows * p.hrow, p.mx ? (size_t)p.hrows * p.srs_I : 0, 4};
   if (bytes) *bytes = sz[which];
   if (block_m) *block_m = p.bm;
   return p.off[segs[which]] + (which == MXMOE_VIEW_STATUS ? kFusedStatusByte : 0);
@@ -395,7 +418,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   const Tuning& tn = tuning();
   if (tn.trace)
     fprintf(stderr, "mxmoe_forward: T=%d H=%d E=%d k=%d I=%d w=%d launcher=%s block_m=%d combine=%s\n",
-            P.T, P.H, P.E, P.k, P.I, s->w_fmt, P.fused ? "one_launch" : (P.large ? "large_m" : "small_m"), P.bm,
+            P.T, P.H, P.E, P.k, P.I, s->w_fmt,
+            P.fused ? "one_launch" : (P.large ? "large_m" : (P.so ? "small_m_slot_order" : "small_m")), P.bm,
             P.combine == 1 ? "slots" : (P.combine == 2 ? "atomic" : "slots_bf16"));
 
   void** ev = opt ? opt->stage_events : nullptr;
@@ -452,6 +476,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   pa.zero_out = slots ? nullptr : out32;
   pa.zero_cnt = P.fuse_final ? done : nullptr;
   pa.n_cnt = P.fuse_final ? P.H / 64 : 0;
+  pa.no_sort = P.so;
   if (e == hipSuccess) e = launch_prologue(pa, s->logits_dtype == MXMOE_F32, aws, st);
   const int n_blocks = P.cap / P.bm;
   GemmParams g{};
@@ -476,6 +501,16 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.out32 = out32;
   g.combine = P.combine;
   g.T = P.T;
+  g.so = P.so;
+  g.so_tiles = P.so_tiles;
+  g.so_cap = P.T;
+  // an expert is without rows with probability about exp(-T k / E): below ~5% the down pass issues
+  // its weights before it reads the count
+  g.so_spec = (long)P.T * P.k > 3L * P.E;
+  g.E = P.E;
+  g.topk_ids = ids;
+  g.so_list = sorted;
+  g.so_cnt = eoff;
   g.xcd_order = tn.xcd_order >= 0 ? tn.xcd_order != 0 : 1;
   g.w_nt = tn.w_nt >= 0 ? tn.w_nt != 0 : 1;
   // large-M unit order: the options' run (-1: one contiguous range per XCD), else the A/B switch,
@@ -506,8 +541,8 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.as = hs;
     dn.a_stride = g.h_stride;
     dn.a_srs = P.srs_I;
-    dn.a_bytes = (uint32_t)((size_t)P.cap * dn.a_stride);
-    dn.as_bytes = (uint32_t)((size_t)P.cap * P.srs_I);
+    dn.a_bytes = (uint32_t)((size_t)P.hrows * dn.a_stride);
+    dn.as_bytes = (uint32_t)((size_t)P.hrows * P.srs_I);
     dn.w = (const uint8_t*)w2_p;
     dn.ws = (const uint8_t*)s2_p;
     dn.xcd_run = unit_run(P.H >= 256 ? 4 * (P.H / 256) : 1, tn.xcd_run_dn);

@@ -28,23 +28,25 @@ namespace mxmoe {
 namespace {
 
 // acc[mt][f][i] is C[row 4g+i of tile mt][column n of fragment f]. Fragments 0/1 are gate/up of
-// intermediate columns chunk*32 + 0..15, fragments 2/3 of chunk*32 + 16..31.
+// intermediate columns chunk*32 + 0..15, fragments 2/3 of chunk*32 + 16..31. hrow[mt][i]: the
+// intermediate row that row 4g+i of tile mt is stored to (its layout row, or its slot in the
+// slot-order plan), -1 for none.
 template <int WF, int MT>
 __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f (&acc)[MT][4],
-                                                 int m0, int r1, int chunk, int n, int g) {
+                                                 const int (&hrow)[MT][4], int chunk, int n) {
   const int ic0 = 32 * chunk;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = m0 + 16 * mt + 4 * g + i;
+      const int rr = hrow[mt][i];
       float a0 = silu(acc[mt][0][i]) * acc[mt][1][i];
       float a1 = silu(acc[mt][2][i]) * acc[mt][3][i];
       if (a_is_fp4(WF)) {  // E2M1 intermediate: 16 bytes per 32 columns, two codes per byte
         const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
         const int se = mx_shared_exp<2>(m);
         const uint32_t b2 = e2m1_pack_pair(a0, a1, se);
-        if (rr < r1) {
+        if (rr >= 0) {
           uint8_t* hr = p.h + (size_t)rr * p.h_stride + ic0 / 2;
           if (!(n & 1)) {
             hr[n / 2] = (uint8_t)b2;
@@ -55,14 +57,14 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
       } else if (WF != WF_BF16) {
         const float m = row16_max(fmaxf(fabsf(a0), fabsf(a1)));
         int se = mx_shared_exp<8>(m);
-        if (rr < r1) {
+        if (rr >= 0) {
           uint8_t* hr = p.h + (size_t)rr * p.h_stride + ic0;
           const uint32_t c2 = e4m3_pair(a0, a1, se);
           hr[n] = (uint8_t)c2;
           hr[16 + n] = (uint8_t)(c2 >> 8);
           if (n == 0) p.hs[(size_t)rr * p.h_srs + chunk] = (uint8_t)(se + 127);
         }
-      } else if (rr < r1) {
+      } else if (rr >= 0) {
         uint16_t* hr = (uint16_t*)(p.h + (size_t)rr * p.h_stride) + ic0;
         hr[n] = (uint16_t)f32_to_bf16_bits(a0);
         hr[16 + n] = (uint16_t)f32_to_bf16_bits(a1);
@@ -73,8 +75,8 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
   if (p.Ip > p.I && 32 * (chunk + 1) == p.I) {
     for (int mt = 0; mt < MT; ++mt)
       for (int i = 0; i < 4; ++i) {
-        const int rr = m0 + 16 * mt + 4 * g + i;
-        if (rr >= r1) continue;
+        const int rr = hrow[mt][i];
+        if (rr < 0) continue;
         if (WF != WF_BF16) {
           const int cb = a_is_fp4(WF) ? 2 : 1;  // codes per byte
           for (int c = p.I / cb + n; c < p.Ip / cb; c += 16) p.h[(size_t)rr * p.h_stride + c] = 0;
@@ -87,6 +89,18 @@ __device__ __forceinline__ void epilogue_gate_up(const GemmParams& p, const v4f 
         }
       }
   }
+}
+
+// Destination rows of the sorted layout: row 4g+i of tile mt is layout row m0 + 16 mt + 4g + i.
+template <int MT>
+__device__ __forceinline__ void layout_rows(int m0, int r1, int g, int (&hrow)[MT][4]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = m0 + 16 * mt + 4 * g + i;
+      hrow[mt][i] = rr < r1 ? rr : -1;
+    }
 }
 
 // Output columns of a down fragment: the prepack interleaves the rows of W2 so that fragment f
@@ -170,45 +184,124 @@ __device__ __forceinline__ void finalize_chunk_if_last(const GemmParams& p, int 
 }
 
 // ------------------------------------------------------------------------------ small-M
+// Slot-order plan: the rows of expert slot es (slot ids in slot order) into rows[], returning
+// their count. A routed expert scans the routing ids, 64 slots per ballot with 16 loads in
+// flight; a token chooses an expert at most once, so it has at most T rows (the host keeps
+// T <= kSlotOrderMaxT). Shared tile j holds the shared slots (slot k of each token) of tokens
+// 16j .. 16j + 15. The order is the sorted layout's (stable by slot), so a tile holds the same
+// rows there and here. Every lane of the wave takes part; the count is wave-uniform.
+__device__ __forceinline__ int so_rows(const GemmParams& p, int es, int lane, int* rows) {
+  if (es >= p.E) {
+    const int t0 = 16 * (es - p.E);
+    const int nr = p.T - t0 < 16 ? p.T - t0 : 16;
+    if (lane < nr) rows[lane] = (t0 + lane) * p.k1 + (p.k1 - 1);
+    return nr;
+  }
+  int cnt = 0;
+  for (int c0 = 0; c0 < p.S; c0 += 64 * 16) {
+    int v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int s = c0 + 64 * j + lane;
+      v[j] = s < p.S ? p.topk_ids[s] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool m = v[j] == es;
+      const uint64_t b = __builtin_amdgcn_ballot_w64(m);
+      const int idx = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+      if (m && idx < kSlotOrderMaxT) rows[idx] = c0 + 64 * j + lane;
+      cnt += __builtin_popcountll(b);
+    }
+  }
+  return cnt < kSlotOrderMaxT ? cnt : kSlotOrderMaxT;
+}
+
+// Slot-order plan, gate_up units of column chunk 0: the expert slot's rows (slot ids, p.S past the
+// count) and, once per expert, its count, for the down pass. Same wave as so_rows.
+__device__ __forceinline__ void so_record(const GemmParams& p, int es, int nr, int lane,
+                                          const int* rows) {
+  if (es < p.E) {
+    int32_t* l = p.so_list + (size_t)es * p.so_cap;
+    for (int i = lane; i < p.so_cap; i += 64) l[i] = i < nr ? rows[i] : p.S;
+    if (lane == 0) p.so_cnt[es] = nr;
+  } else {
+    const int t0 = 16 * (es - p.E);
+    if (lane < nr) p.so_list[(size_t)p.E * p.so_cap + t0 + lane] = rows[lane];
+    if (lane == 0 && t0 == 0) p.so_cnt[p.E] = p.T;
+  }
+}
+
 // KS > 1 (few units, 16-row blocks): KS waves share a unit, wave w taking K-steps w, w + KS, ...;
 // their accumulators are added in LDS in wave order (a fixed order) and wave 0 runs the epilogue.
 // With a few hundred single-wave units (a handful of tokens) each wave's K stream is a chain of
 // memory round trips; split over KS waves the chain is KS times shorter.
-template <int WF, int MT, bool GATE_UP, int D, int KS, int AUX = 0>
+// SO: the slot-order plan (one wave per unit, one 16-row tile at a time).
+template <int WF, int MT, bool GATE_UP, int D, int KS, int AUX = 0, bool SO = false>
 __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chunks, int n_blocks) {
   static_assert(GATE_UP || MT == 1, "the down epilogue of this launcher handles one 16-row tile");
   static_assert(KS == 1 || MT == 1, "split K reduces one 16-row tile");
+  static_assert(!SO || (KS == 1 && MT == 1), "slot order: one wave, one 16-row tile");
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int wave = KS > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   // Unit order: XCD x = blockIdx % 8 takes the x-th contiguous range of the units that have rows
   // (the grid is sized for the layout's capacity; ranges cut from the real tile count give every
   // XCD the same work, measured 57.9 -> 55.6 us for the 32-token gate_up); units run chunk-major,
   // tiles fastest, so the tiles of one expert on one chunk share an XCD.
-  const int nb = *p.num_post_pad / p.block_m;
+  const int nb = SO ? p.E + p.so_tiles : *p.num_post_pad / p.block_m;
   const int total = n_chunks * nb;
   const int per_xcd = (total + 7) >> 3;
   if (p.xcd_order && (int)(blockIdx.x >> 3) >= per_xcd) return;
   const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
   if (u >= total) return;
   const int chunk = u / nb, blk = u - chunk * nb;
-  const int r0 = blk * p.block_m;
-  const int e = p.block_expert[blk];
-  const int r1 = r0 + p.block_m;
+  // slot order: rows r0 .. r1 - 1 of the unit are so_r[r] (slot ids)
+  __shared__ int so_r[SO ? kSlotOrderMaxT : 1];
+  int r0, r1, e;
   TileRows<MT> tr;
-  tile_weights<WF, MT>(p, e, chunk * 4, tr);
+  // Register ring of D stages; the host picks D dividing NKS, so the steady-state loop issues
+  // the loads of group k0 + D while multiplying group k0 without any branch, and the last group
+  // is peeled. Weight loads of the first group go out before the (dependent) row lookup.
+  Stage<WF, MT> buf[D];
+  if constexpr (SO) {
+    // the unit's expert is known: its first weight K-steps go out before the scan for its rows
+    // (an expert without rows then drops D K-steps of one chunk)
+    e = blk < p.E ? blk : p.E;
+    tile_weights<WF, MT>(p, e, chunk * 4, tr);
+#pragma unroll
+    for (int s = 0; s < D; ++s) load_b<WF, MT, MT, AUX>(p, tr, s, lane, buf[s]);
+    r0 = 0;
+    r1 = so_rows(p, blk, lane, so_r);
+    if (GATE_UP && chunk == 0) so_record(p, blk, r1, lane, so_r);
+    if (r1 == 0) {  // wave-uniform
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+  } else {
+    r0 = blk * p.block_m;
+    e = p.block_expert[blk];
+    r1 = r0 + p.block_m;
+    tile_weights<WF, MT>(p, e, chunk * 4, tr);
+  }
+  // slot id of unit row r (p.S: none)
+  auto row_slot = [&](int r) -> int {
+    if constexpr (SO) return r < r1 ? so_r[r] : p.S;
+    else return r < r1 ? p.sorted_ids[r] : p.S;
+  };
+  // slot order: intermediate row of unit row r (the expert's rows, then the shared tile's offset)
+  const int hbase = SO ? e * p.so_cap + (blk < p.E ? 0 : 16 * (blk - p.E)) : 0;
   for (int m0 = r0; m0 < r1; m0 += 16 * MT) {
     v4f acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-    // Register ring of D stages; the host picks D dividing NKS, so the steady-state loop issues
-    // the loads of group k0 + D while multiplying group k0 without any branch, and the last group
-    // is peeled. Weight loads of the first group go out before the (dependent) row lookup.
-    Stage<WF, MT> buf[D];
     const int nk = p.NKS / KS;  // K-steps of this wave: global step wave + KS * i
+    if (!SO || m0 != r0) {  // slot order: the first tile's ring went out before the scan
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_b<WF, MT, MT, AUX>(p, tr, wave + KS * s, lane, buf[s]);
+      for (int s = 0; s < D; ++s) load_b<WF, MT, MT, AUX>(p, tr, wave + KS * s, lane, buf[s]);
+    }
     // down: slot id and routing weight of the lane's four output rows, fetched now so the
     // epilogue does not wait for them
     int rsid[4];
@@ -216,11 +309,19 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
     if (!GATE_UP) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        rsid[i] = p.sorted_ids[m0 + 4 * g + i];
-        rw[i] = p.sorted_w[m0 + 4 * g + i];
+        rsid[i] = row_slot(m0 + 4 * g + i);
+        if constexpr (SO) rw[i] = rsid[i] < p.S ? p.topk_w[rsid[i]] : 0.0f;
+        else rw[i] = p.sorted_w[m0 + 4 * g + i];
       }
     }
-    tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
+    if constexpr (SO) {  // gate_up: token row of the slot; down: the expert's intermediate row
+      const int sid = row_slot(m0 + n);
+      const int ar = GATE_UP ? sid / p.k1 : hbase + m0 + n;
+      tr.aoff[0] = sid < p.S ? (uint32_t)ar * (uint32_t)p.a_stride + 16u * g : kOutOfRange;
+      tr.asoff[0] = sid < p.S ? (uint32_t)ar * (uint32_t)p.a_srs : kOutOfRange;
+    } else {
+      tile_act_rows<WF, MT, GATE_UP>(p, m0, r1, n, g, tr);
+    }
 #pragma unroll
     for (int s = 0; s < D; ++s) load_a<WF, MT>(tr, wave + KS * s, buf[s]);
     int k0 = 0;
@@ -250,15 +351,29 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
         acc[0][f] = t;
       }
     }
-    if constexpr (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
-    else epilogue_down_rows(p, acc[0], rsid, rw, chunk, n);
+    if constexpr (GATE_UP) {
+      int hrow[MT][4];
+      if constexpr (SO) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + 4 * g + i;
+          hrow[0][i] = r < r1 ? hbase + r : -1;
+        }
+      } else {
+        layout_rows<MT>(m0, r1, g, hrow);
+      }
+      epilogue_gate_up<WF, MT>(p, acc, hrow, chunk, n);
+    } else {
+      epilogue_down_rows(p, acc[0], rsid, rw, chunk, n);
+    }
   }
-  if (!GATE_UP && p.y) finalize_chunk_if_last(p, chunk, lane);
+  if (!SO && !GATE_UP && p.y) finalize_chunk_if_last(p, chunk, lane);
 }
 
 // Small-M down pass with the 16-row activation tile shared by a workgroup: its 4 waves take 4
-// consecutive 64-column chunks of one tile of the sorted layout, and the tile's intermediate rows
-// (16 rows of Ip codes and their scale bytes, contiguous in the layout) are copied into LDS once
+// consecutive 64-column chunks of one tile of the sorted layout (slot order: of one expert slot,
+// its tiles in turn), and the tile's intermediate rows (16 rows of Ip codes and their scale bytes,
+// contiguous in the layout, gathered by slot in slot order) are copied into LDS once
 // instead of being gathered by every wave at every K-step; each wave then streams its own weight
 // slice through the same register ring as k_gemm_stream, and the sums are the same (same K order
 // per wave, no split). At decode the activation loads were a third of the down pass's vector-memory
@@ -273,7 +388,7 @@ __host__ __device__ inline int sa_lds_bytes(int a_stride, int a_srs) {
   return 16 * sa_pitch(a_stride) + 16 * a_srs;
 }
 
-template <int WF, int D, int AUX>
+template <int WF, int D, int AUX, bool SO = false>
 __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sa_lds[];
   constexpr bool A4 = a_is_fp4(WF);
@@ -281,7 +396,7 @@ __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, in
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // unit (chunk group, tile), chunk-group-major, in contiguous per-XCD ranges (as k_gemm_stream)
-  const int nb = *p.num_post_pad / 16;
+  const int nb = SO ? p.E + p.so_tiles : *p.num_post_pad / 16;
   const int total = n_groups * nb;
   const int per_xcd = (total + 7) >> 3;
   if (p.xcd_order && (int)(blockIdx.x >> 3) >= per_xcd) return;
@@ -289,73 +404,131 @@ __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, in
   if (u >= total) return;  // uniform over the workgroup
   const int grp = u / nb, blk = u - grp * nb;
   const int chunk = grp * kSaWaves + wave;
-  const int r0 = blk * 16;
-  const int e = p.block_expert[blk];
+  // Rows: sorted layout, the 16-row tile r0 of the layout; slot order, the expert slot's
+  // intermediate rows hbase, hbase + 1, ... (its count from gate_up, or the shared tile's tokens),
+  // the first tile copied before the count is known (rows past it are never stored).
+  int e, r0, cnt, hbase, t0 = 0;
+  if constexpr (SO) {
+    e = blk < p.E ? blk : p.E;
+    if (blk < p.E) {
+      cnt = p.so_cnt[e];
+      hbase = e * p.so_cap;
+    } else {
+      t0 = 16 * (blk - p.E);
+      cnt = p.T - t0 < 16 ? p.T - t0 : 16;
+      hbase = p.E * p.so_cap + t0;
+    }
+    r0 = 0;
+  } else {
+    r0 = blk * 16;
+    cnt = 16;
+    hbase = 0;
+    e = p.block_expert[blk];
+  }
   TileRows<1> tr;
   tile_weights<WF, 1>(p, e, chunk * 4, tr);
-  Stage<WF, 1> buf[D];
-#pragma unroll
-  for (int s = 0; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
-  int rsid[4];
-  float rw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rsid[i] = p.sorted_ids[r0 + 4 * g + i];
-    rw[i] = p.sorted_w[r0 + 4 * g + i];
-  }
-  // the tile's rows and scale rows into LDS: 16-byte pieces, every load of a batch issued before
-  // the first LDS store
   const int pitch = sa_pitch(p.a_stride);
   const int cbytes = 16 * p.a_stride, sbytes = 16 * p.a_srs;
   const __amdgpu_buffer_rsrc_t ra = raw_rsrc(p.a, p.a_bytes);
   const __amdgpu_buffer_rsrc_t ras = raw_rsrc(p.as, p.as_bytes);
-  const uint32_t a0 = (uint32_t)r0 * (uint32_t)p.a_stride, s0 = (uint32_t)r0 * (uint32_t)p.a_srs;
-  constexpr int kB = 4;
-  for (int base = 16 * threadIdx.x; base < cbytes + sbytes; base += 16 * 64 * kSaWaves * kB) {
-    v4i v[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int o = base + 16 * 64 * kSaWaves * j;
-      v[j] = o < cbytes ? __builtin_amdgcn_raw_buffer_load_b128(ra, a0 + o, 0, 0)
-                        : __builtin_amdgcn_raw_buffer_load_b128(ras, o < cbytes + sbytes ? s0 + (o - cbytes) : kOutOfRange, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const int o = base + 16 * 64 * kSaWaves * j;
-      if (o < cbytes) {
-        const int row = o / p.a_stride, col = o - row * p.a_stride;
-        *(v4i*)(sa_lds + row * pitch + col) = v[j];
-      } else if (o < cbytes + sbytes) {
-        *(v4i*)(sa_lds + 16 * pitch + (o - cbytes)) = v[j];
-      }
-    }
-  }
-  __syncthreads();
   const uint8_t* arow = sa_lds + n * pitch;
   const uint32_t* srow = (const uint32_t*)(sa_lds + 16 * pitch + n * p.a_srs);
-  v4f acc[4];
+  // The first tile's row copy goes out before the count is read. Its weights go out with it when
+  // few experts lack rows (so_spec), else after the count: an expert without rows then reads none
+  // (at three K-steps a unit's ring is its whole weight slice). Measured: 32 tokens over 128
+  // experts (13% without rows) down 28.5 us weights-after against 30.1 us weights-first; 128
+  // tokens MXFP4 36.6 against 35.0 us.
+  const bool spec = !SO || p.so_spec;
+  for (int m0 = 0;; m0 += 16) {
+    Stage<WF, 1> buf[D];
+    if (spec || m0 > 0) {
 #pragma unroll
-  for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto mma_step = [&](int ks, const Stage<WF, 1>& st) {
-    v8i a8;
-    a8.lo = *(const v4i*)(arow + ks * SB + 16 * g);
-    a8.hi = A4 ? v4i{0, 0, 0, 0} : *(const v4i*)(arow + ks * SB + 64 + 16 * g);
-    const uint32_t sa = srow[ks];
-    mma_frags<WF>(a8, (int)(sa >> (8 * g)), st.b, (int)st.sb, acc);
-  };
-  const int nk = p.NKS;
-  int k0 = 0;
-  for (; k0 + D < nk; k0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      mma_step(k0 + s, buf[s]);
-      load_b<WF, 1, 1, AUX>(p, tr, k0 + s + D, lane, buf[s]);
+      for (int s = 0; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
     }
-  }
+    // slot of each of the lane's four output rows (p.S: none)
+    int rsid[4];
+    float rw[4];
 #pragma unroll
-  for (int s = 0; s < D; ++s) mma_step(k0 + s, buf[s]);
-  epilogue_down_rows(p, acc, rsid, rw, chunk, n);
-  if (p.y) finalize_chunk_if_last(p, chunk, lane);
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + 4 * g + i;
+      if constexpr (SO) {
+        if (blk < p.E) rsid[i] = p.so_list[hbase + (r < p.so_cap ? r : 0)];
+        else rsid[i] = t0 + r < p.T ? (t0 + r) * p.k1 + (p.k1 - 1) : p.S;
+      } else {
+        rsid[i] = p.sorted_ids[r0 + r];
+        rw[i] = p.sorted_w[r0 + r];
+      }
+    }
+    // The tile's rows and scale rows into LDS (16 consecutive rows), in 16-byte pieces, every load
+    // of a batch issued before the first LDS store.
+    const uint32_t a0 = (uint32_t)(r0 + hbase + m0) * (uint32_t)p.a_stride;
+    const uint32_t s0 = (uint32_t)(r0 + hbase + m0) * (uint32_t)p.a_srs;
+    constexpr int kB = 4;
+    for (int base = 16 * threadIdx.x; base < cbytes + sbytes; base += 16 * 64 * kSaWaves * kB) {
+      v4i v[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int o = base + 16 * 64 * kSaWaves * j;
+        v[j] = o < cbytes ? __builtin_amdgcn_raw_buffer_load_b128(ra, a0 + o, 0, 0)
+                          : __builtin_amdgcn_raw_buffer_load_b128(ras, o < cbytes + sbytes ? s0 + (o - cbytes) : kOutOfRange, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int o = base + 16 * 64 * kSaWaves * j;
+        if (o < cbytes) {
+          const int row = o / p.a_stride, col = o - row * p.a_stride;
+          *(v4i*)(sa_lds + row * pitch + col) = v[j];
+        } else if (o < cbytes + sbytes) {
+          *(v4i*)(sa_lds + 16 * pitch + (o - cbytes)) = v[j];
+        }
+      }
+    }
+    if constexpr (SO) {
+      if (m0 == 0) {
+        if (cnt == 0) {  // an expert without rows (uniform over the workgroup)
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          return;
+        }
+        if (!spec) {
+#pragma unroll
+          for (int s = 0; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (SO) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (m0 + 4 * g + i >= cnt) rsid[i] = p.S;  // list entries past the count
+        rw[i] = rsid[i] < p.S ? p.topk_w[rsid[i]] : 0.0f;
+      }
+    }
+    v4f acc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[f] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto mma_step = [&](int ks, const Stage<WF, 1>& st) {
+      v8i a8;
+      a8.lo = *(const v4i*)(arow + ks * SB + 16 * g);
+      a8.hi = A4 ? v4i{0, 0, 0, 0} : *(const v4i*)(arow + ks * SB + 64 + 16 * g);
+      const uint32_t sa = srow[ks];
+      mma_frags<WF>(a8, (int)(sa >> (8 * g)), st.b, (int)st.sb, acc);
+    };
+    const int nk = p.NKS;
+    int k0 = 0;
+    for (; k0 + D < nk; k0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        mma_step(k0 + s, buf[s]);
+        load_b<WF, 1, 1, AUX>(p, tr, k0 + s + D, lane, buf[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < D; ++s) mma_step(k0 + s, buf[s]);
+    epilogue_down_rows(p, acc, rsid, rw, chunk, n);
+    if (m0 + 16 >= cnt) break;
+    __syncthreads();  // every wave's reads of this tile come before the next tile's copy
+  }
+  if (!SO && p.y) finalize_chunk_if_last(p, chunk, lane);
 }
 
 // ------------------------------------------------------------------------------ large-M
@@ -748,7 +921,11 @@ __global__ __launch_bounds__(64) void k_gemm_direct(GemmParams p) {
       mma_stage<WF, MT>(cur, 8 * g, acc);
       if (ks + 1 < p.NKS) cur = nxt;
     }
-    if (GATE_UP) epilogue_gate_up<WF, MT>(p, acc, m0, r1, chunk, n, g);
+    if (GATE_UP) {
+      int hrow[MT][4];
+      layout_rows<MT>(m0, r1, g, hrow);
+      epilogue_gate_up<WF, MT>(p, acc, hrow, chunk, n);
+    }
     else epilogue_down<MT>(p, acc, m0, r1, chunk, n, g);
   }
 }
@@ -785,31 +962,56 @@ inline bool tile_pipe(bool gate_up, int wf) {
   return gate_up || w_is_fp4(wf);
 }
 
-template <int WF, bool GATE_UP, int D, int KS = 1>
+// n_blocks: the layout's tile capacity, or the expert slots of the slot-order plan
+template <int WF, bool GATE_UP, int D, int KS = 1, bool SO = false>
 hipError_t launch_stream(const GemmParams& p, int n_chunks, int n_blocks, hipStream_t st) {
   const int total = n_chunks * n_blocks;
   const int grid = ((total + 7) / 8) * 8;
   if (p.w_nt)
-    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, kNonTemporal>), dim3(grid),
+    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, kNonTemporal, SO>), dim3(grid),
                        dim3(64 * KS), 0, st, p, n_chunks, n_blocks);
   else
-    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS>), dim3(grid), dim3(64 * KS), 0, st,
-                       p, n_chunks, n_blocks);
+    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, 0, SO>), dim3(grid), dim3(64 * KS),
+                       0, st, p, n_chunks, n_blocks);
   return hipGetLastError();
 }
 
-template <int WF, int D>
+template <int WF, int D, bool SO = false>
 hipError_t launch_down_sa(const GemmParams& p, int n_groups, int n_blocks, hipStream_t st) {
   const int total = n_groups * n_blocks;
   const int grid = ((total + 7) / 8) * 8;
   const size_t lds = (size_t)sa_lds_bytes(p.a_stride, p.a_srs);
   if (p.w_nt)
-    hipLaunchKernelGGL((k_gemm_down_sa<WF, D, kNonTemporal>), dim3(grid), dim3(64 * kSaWaves), lds,
-                       st, p, n_groups);
+    hipLaunchKernelGGL((k_gemm_down_sa<WF, D, kNonTemporal, SO>), dim3(grid), dim3(64 * kSaWaves),
+                       lds, st, p, n_groups);
   else
-    hipLaunchKernelGGL((k_gemm_down_sa<WF, D, 0>), dim3(grid), dim3(64 * kSaWaves), lds, st, p,
-                       n_groups);
+    hipLaunchKernelGGL((k_gemm_down_sa<WF, D, 0, SO>), dim3(grid), dim3(64 * kSaWaves), lds, st,
+                       p, n_groups);
   return hipGetLastError();
+}
+
+// The slot-order plan: units over (column chunk, expert slot); the down pass shares its tiles
+// across four column chunks where the shape allows, as in the sorted plan.
+template <int WF, bool GATE_UP>
+hipError_t launch_slot_order(const GemmParams& p, int n_chunks, hipStream_t st) {
+  const int ns = p.E + p.so_tiles;
+  const int d = stream_depth(WF, p.NKS);
+  if constexpr (!GATE_UP && WF != WF_BF16) {
+    if (n_chunks % kSaWaves == 0 && sa_lds_bytes(p.a_stride, p.a_srs) <= kSaMaxLds) {
+      switch (d) {
+        case 4: return launch_down_sa<WF, 4, true>(p, n_chunks / kSaWaves, ns, st);
+        case 3: return launch_down_sa<WF, 3, true>(p, n_chunks / kSaWaves, ns, st);
+        case 2: return launch_down_sa<WF, 2, true>(p, n_chunks / kSaWaves, ns, st);
+        default: return launch_down_sa<WF, 1, true>(p, n_chunks / kSaWaves, ns, st);
+      }
+    }
+  }
+  switch (d) {
+    case 4: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 4), 1, true>(p, n_chunks, ns, st);
+    case 3: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 3), 1, true>(p, n_chunks, ns, st);
+    case 2: return launch_stream<WF, GATE_UP, 2, 1, true>(p, n_chunks, ns, st);
+    default: return launch_stream<WF, GATE_UP, 1, 1, true>(p, n_chunks, ns, st);
+  }
 }
 
 template <int WF, bool GATE_UP>
@@ -842,6 +1044,7 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
     }
     return hipGetLastError();
   }
+  if (p.so) return launch_slot_order<WF, GATE_UP>(p, n_chunks, st);
   // Split K over 4 waves when the layout has fewer 16-row tiles than a quarter of the SIMDs' share
   // (a handful of tokens) and each wave keeps whole ring groups.
   if (WF != WF_BF16 && p.block_m == 16 && n_chunks * n_blocks <= kSplitKMaxUnits &&
@@ -884,6 +1087,11 @@ hipError_t launch_wf(int wf, bool large, const GemmParams& p, int n_blocks, hipS
 }
 
 }  // namespace
+
+bool slot_order_fits(int T, int E, int top_k, int I) {
+  const int S = T * (top_k + 1), E1 = E + 1;
+  return T <= kSlotOrderMaxT && S >= E1 && (size_t)E1 * (I / 32) > (size_t)kSplitKMaxUnits;
+}
 
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int n_blocks, hipStream_t st) {
   return launch_wf<true>(wf, large, p, n_blocks, st);

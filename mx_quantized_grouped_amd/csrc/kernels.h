@@ -26,6 +26,7 @@ struct Tuning {
   int stream_depth;    // MXMOE_STREAM_DEPTH: small-M register ring depth 1..4
   int prio;            // MXMOE_PRIO: raised wave priority during the large-M MFMAs (0/1)
   int tile_pipe;       // MXMOE_TILE_PIPE: pipelined large-M K-steps (0/1)
+  int slot_order;      // MXMOE_SLOT_ORDER: 0 = automatic plans never take the slot-order plan
   int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
   int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
 };
@@ -75,6 +76,7 @@ struct PrologueArgs {
   float* zero_out;  // null: nothing to clear
   int32_t* zero_cnt;  // n_cnt counters to clear (null: none)
   int n_cnt;
+  bool no_sort;     // slot-order plan: routing and quantisation only
 };
 hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_scratch,
                            hipStream_t st);
@@ -137,7 +139,26 @@ struct GemmParams {
   // order over the grid; 0: one contiguous range per XCD)
   int xcd_run;
   int w_nt;  // small-M launcher: weight loads with the non-temporal hint
+  // Slot-order plan (small-M launcher, no sort): so != 0. A unit is (column chunk, expert slot):
+  // slots [0, E) are the routed experts, slots [E, E + so_tiles) the shared expert's tiles of 16
+  // consecutive tokens. Every expert owns so_cap = T intermediate rows (expert-major, row
+  // e * so_cap + i for its i-th slot in slot order). gate_up's units find a routed expert's slots
+  // by a scan of topk_ids, and its chunk-0 unit records them in so_list[e * so_cap + i] (p.S past
+  // the count) and their count in so_cnt[e], which the down pass reads instead of scanning again.
+  int so, so_tiles, so_cap, E;
+  int so_spec;  // down: weight loads before the expert's count is known (few experts without rows)
+  const int32_t* topk_ids;
+  int32_t* so_list;
+  int32_t* so_cnt;
 };
+// Most tokens of a slot-order plan (rows of one expert, held in LDS by each unit).
+constexpr int kSlotOrderMaxT = 256;
+// Most intermediate bytes (T rows per expert) the automatic choice gives a slot-order plan.
+constexpr size_t kSlotOrderMaxRowBytes = 64u << 20;
+// Whether the small-M plan of this shape runs in slot order: enough slots that most experts have
+// rows (a unit of an empty expert only scans the ids), at most kSlotOrderMaxT tokens, and enough
+// gate_up units that K is not split.
+bool slot_order_fits(int T, int E, int top_k, int I);
 hipError_t launch_gate_up(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 hipError_t launch_down(int wf, bool large, const GemmParams& p, int grid_y, hipStream_t st);
 

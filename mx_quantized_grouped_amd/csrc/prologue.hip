@@ -8,6 +8,7 @@
 //     accumulator when that combine is used).
 //   more tokens: one launch routes (one wave per token, 16 per workgroup) and quantises, then the
 //     sort: one workgroup up to 4096 slots, the three-pass sort beyond.
+//   slot-order plan (no sorted layout): the routing and quantising launch alone.
 #include "align_dev.h"
 #include "device.h"
 #include "kernels.h"
@@ -86,11 +87,13 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
   const int S = a.T * (a.top_k + 1);
   const bool work = a.xq || a.zero_out;
   const int nq = work ? (int)(((size_t)a.T * (a.H / 32) * 4 + kThreads - 1) / kThreads) : 0;
+  // Slot-order plan: no sort; routing spreads over workgroups (a wave per token) beside the
+  // quantisation.
   // One launch while one workgroup's 16 waves route every token two at most each: a wave routes a
   // token in about 1.7 us, so at 32 tokens the fused kernel (about 11.4 us) still beats a routing
   // launch plus a sort launch (about 12.9 us with the gap between them); beyond that, routing
   // spreads over workgroups and the sort becomes a launch of its own.
-  if (S <= kAlignSmallMaxSlots && a.T <= 2 * (kThreads / 64)) {
+  if (!a.no_sort && S <= kAlignSmallMaxSlots && a.T <= 2 * (kThreads / 64)) {
     dim3 grid(1 + nq), block(kThreads);
     if (logits_f32) hipLaunchKernelGGL(k_prologue_small<true>, grid, block, 0, st, a);
     else hipLaunchKernelGGL(k_prologue_small<false>, grid, block, 0, st, a);
@@ -101,7 +104,7 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
   if (logits_f32) hipLaunchKernelGGL(k_route_quant<true>, grid, block, 0, st, a, nr);
   else hipLaunchKernelGGL(k_route_quant<false>, grid, block, 0, st, a, nr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.no_sort) return e;
   return launch_align(a.ids, a.T, a.E, a.top_k, a.block_m, a.out, align_scratch, st);
 }
 

@@ -160,10 +160,11 @@ def test_workspace_view(L):
     assert nb == 32 * 96                                 # 3072 / 32 scale bytes, already 16-aligned
     sb = B.Shape.of(16, 256, 8, 2, 128, "bf16")
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_XQ)[1] == 0   # bf16 weights: no activation codes
-    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_H)
+    srt = B.Options(0, 0, 0, 0, None, 0, 0, 0, B.MXMOE_LAYOUT_SORTED)
+    off, nb, _ = B.mxmoe_workspace_view(s, srt, B.VIEW_H)
     cap = L.mxmoe_align_capacity(32, 128, 8, 16)
     assert nb == cap * 384 and off % 256 == 0            # I = 384 is three whole 128-K steps
-    off, nb, _ = B.mxmoe_workspace_view(s, None, B.VIEW_HS)
+    off, nb, _ = B.mxmoe_workspace_view(s, srt, B.VIEW_HS)
     assert nb == cap * 16                                # 12 scale bytes padded to 16
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_H)[1] == L.mxmoe_align_capacity(16, 8, 2, 16) * 128 * 2
     assert B.mxmoe_workspace_view(sb, None, B.VIEW_HS)[1] == 0
@@ -204,8 +205,55 @@ def test_options_one_launch(L):
     assert B.mxmoe_workspace_bytes(dec, B.Options(2, 0, 0, 0, None, 1)) == 0
     # invalid values
     for o in [B.Options(0, 0, 0, 0, None, 2), B.Options(0, 0, 0, 0, None, 0, -1),
-              B.Options(0, 0, 0, 0, None, 0, 0, 2), B.Options(0, 0, 0, 0, None, 0, 0, 0, 1)]:
+              B.Options(0, 0, 0, 0, None, 0, 0, 2), B.Options(0, 0, 0, 0, None, 0, 0, 0, 3)]:
         assert B.mxmoe_workspace_bytes(dec, o) == 0
+
+
+def _layout(shape, o=None):
+    """'slots' for the slot-order plan (no tile map: views 3-5 are empty), else 'sorted'."""
+    return "sorted" if B.mxmoe_workspace_view(shape, o, B.VIEW_BLOCK_EXPERT)[1] else "slots"
+
+
+def test_options_layout(L):
+    dec = B.Shape.of(32, 3072, 128, 8, 384, "mxfp8")
+    slots = lambda *a: B.Options(*a, 0, None, 0, 0, 0, B.MXMOE_LAYOUT_SLOTS)
+    sorted_ = B.Options(0, 0, 0, 0, None, 0, 0, 0, B.MXMOE_LAYOUT_SORTED)
+    # automatic: slot order at decode over 128 experts (288 slots, 129 experts; 12 x 129 gate_up
+    # units); the sorted layout for one or six tokens over 512 experts (fewer slots than experts),
+    # small expert counts (few units: K is split), large batches and the atomic combine
+    assert _layout(dec) == "slots"
+    assert _layout(B.Shape.of(128, 3072, 128, 8, 768, "mxfp4", act_fmt="mxfp4")) == "slots"
+    assert _layout(B.Shape.of(1, 2048, 512, 8, 512, "mxfp4")) == "sorted"
+    assert _layout(B.Shape.of(6, 2048, 512, 8, 512, "mxfp4")) == "sorted"
+    assert _layout(B.Shape.of(16, 256, 8, 2, 128, "bf16")) == "sorted"
+    assert _layout(B.Shape.of(8192, 3072, 128, 8, 384, "mxfp8")) == "sorted"
+    assert _layout(dec, B.Options(0, 2, 0, 0)) == "sorted"
+    assert _layout(dec, sorted_) == "sorted"
+    # the one-launch path has its own layout
+    assert _layout(dec, B.Options(0, 0, 0, 0, None, 1)) == "sorted"
+    # required: any small-M plan with 16-row tiles, a slot-row combine and at most 256 tokens
+    assert _layout(dec, slots(0, 0, 0)) == "slots"
+    assert _layout(B.Shape.of(1, 2048, 512, 8, 512, "mxfp4"), slots(1, 3, 16)) == "slots"
+    assert B.mxmoe_workspace_view(dec, slots(0, 0, 0), B.VIEW_SORTED_IDS)[2] == 16
+    for bad in [slots(2, 0, 0), slots(0, 2, 0), slots(1, 0, 32)]:
+        assert B.mxmoe_workspace_bytes(dec, bad) == 0
+    assert B.mxmoe_workspace_bytes(dec.with_T(257), slots(1, 0, 0)) == 0
+    assert B.mxmoe_workspace_bytes(dec.with_T(256), slots(1, 0, 0)) > 0
+    assert B.mxmoe_workspace_bytes(dec, B.Options(0, 0, 0, 0, None, 1, 0, 0, 2)) == 0
+    # slot order: T intermediate rows and T list entries per expert (shared one included)
+    assert B.mxmoe_workspace_view(dec, slots(0, 0, 0), B.VIEW_H)[1] == 129 * 32 * 384
+    assert B.mxmoe_workspace_view(dec, slots(0, 0, 0), B.VIEW_HS)[1] == 129 * 32 * 16
+    assert B.mxmoe_workspace_view(dec, slots(0, 0, 0), B.VIEW_SORTED_IDS)[1] == 129 * 32 * 4
+    for v in (B.VIEW_BLOCK_EXPERT, B.VIEW_NUM_POST_PAD, B.VIEW_EXPERT_OFF):
+        assert B.mxmoe_workspace_view(dec, slots(0, 0, 0), v)[1] == 0
+    # at least the sorted layout's capacity: one token over 512 experts (144 rows) takes 513
+    one = B.Shape.of(1, 2048, 512, 8, 512, "mxfp4")
+    assert L.mxmoe_align_capacity(1, 512, 8, 16) < 513
+    assert B.mxmoe_workspace_view(one, slots(1, 3, 16), B.VIEW_H)[1] == 513 * 512
+    # the automatic choice keeps T rows per expert within 64 MiB: 256 tokens over 256 experts at
+    # I = 2048 (257 * 256 * 2048 bytes) stays sorted, unless asked for
+    big = B.Shape.of(256, 2048, 256, 8, 2048, "mxfp8")
+    assert _layout(big) == "sorted" and _layout(big, slots(1, 1, 0)) == "slots"
 
 
 def test_auto_launcher_thresholds(L):

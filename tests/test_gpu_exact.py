@@ -11,7 +11,8 @@ quantised intermediate (codes and scale bytes) must equal the oracle's Q2 of the
 transposed fragment, a wrong scale byte, a swapped gate/up tile or a misplaced output row changes
 an exact value and fails here, where the output tolerance alone might absorb it.
 
-Paths covered: the small-M streaming launcher (with split K over four waves at H = 512), the
+Paths covered: the small-M streaming launcher (with split K over four waves at H = 512; sorted
+and slot-order row layouts), the
 large-M tile launcher (128- and 256-row layout blocks), the one-wave large-M launcher (other tile
 heights, and the down pass when H/64 is not a multiple of 4), fp8, fp4 and bf16 weights, MXFP4
 weights with MXFP4 activations and intermediate (W4A4), fp32 slot rows and the atomic combine. bf16 slot rows (one rounding per slot) are not exact and are
@@ -39,7 +40,8 @@ CASES = [  # T, H, E, top_k, I, weight format
     (24, 512, 8, 2, 256, "w4a4"),     # MXFP4 weights and activations
     (300, 256, 4, 2, 128, "w4a4"),
 ]
-OPTIONS = [None, (1, 1, 0), (1, 2, 0), (2, 1, 0), (2, 2, 0), (2, 1, 32), (2, 1, 256), "one_launch"]
+OPTIONS = [None, (1, 1, 0), (1, 2, 0), (2, 1, 0), (2, 2, 0), (2, 1, 32), (2, 1, 256), "one_launch",
+           "slot_order"]
 
 
 def _say(*a):
@@ -128,6 +130,10 @@ def test_exact_output_and_intermediate(case, opt):
         if c["fmt"] in ("bf16", "w4a4") or c["T"] > 128:
             pytest.skip("the one-launch path takes MX weights, E4M3 activations, up to 128 tokens")
         o = B.Options(0, 0, 0, 0, None, 1)
+    elif opt == "slot_order":
+        if c["T"] > 256:
+            pytest.skip("the slot-order plan takes at most 256 tokens")
+        o = B.Options(1, 1, 0, 0, None, 0, 0, 0, B.MXMOE_LAYOUT_SLOTS)
     else:
         o = None if opt is None else B.Options(opt[0], opt[1], opt[2], 0)
     _say("forward", c["shape"].T, c["shape"].H, c["fmt"], opt)
@@ -150,11 +156,15 @@ def test_exact_output_and_intermediate(case, opt):
     T, k1, I = c["T"], c["k"] + 1, c["I"]
     S = T * k1
     sids, _ = _view(ws, c["shape"], o, B.VIEW_SORTED_IDS, torch.int32)
-    npp = int(_view(ws, c["shape"], o, B.VIEW_NUM_POST_PAD, torch.int32)[0][0])
+    npp_v, _ = _view(ws, c["shape"], o, B.VIEW_NUM_POST_PAD, torch.int32)
+    # slot order: no tile map; T rows per expert, entries past an expert's count hold S
+    npp = int(npp_v[0]) if len(npp_v) else len(sids)
+    Ip = (I + 127) // 128 * 128
+    hrow = {"bf16": 2 * Ip, "w4a4": Ip // 2}.get(c["fmt"], Ip)   # bytes of an intermediate row
     inter = c["ref"].extras["intermediate"]
     if c["fmt"] == "bf16":
         h, _ = _view(ws, c["shape"], o, B.VIEW_H, torch.int16)
-        h = h.view(np.uint16).reshape(len(sids), -1)
+        h = h.view(np.uint16).reshape(-1, hrow // 2)
         for r in range(npp):
             f = int(sids[r])
             if f < S:
@@ -162,8 +172,8 @@ def test_exact_output_and_intermediate(case, opt):
         return
     h, _ = _view(ws, c["shape"], o, B.VIEW_H, torch.uint8)
     hs, _ = _view(ws, c["shape"], o, B.VIEW_HS, torch.uint8)
-    h = h.reshape(len(sids), -1)
-    hs = hs.reshape(len(sids), -1)
+    h = h.reshape(-1, hrow)
+    hs = hs.reshape(h.shape[0], -1)
     a4 = c["fmt"] == "w4a4"
     n = 0
     for r in range(npp):
