@@ -434,16 +434,19 @@ __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, in
   const uint8_t* arow = sa_lds + n * pitch;
   const uint32_t* srow = (const uint32_t*)(sa_lds + 16 * pitch + n * p.a_srs);
   // The first tile's row copy goes out before the count is read. Its weights go out with it when
-  // few experts lack rows (so_spec), else after the count: an expert without rows then reads none
-  // (at three K-steps a unit's ring is its whole weight slice). Measured: 32 tokens over 128
-  // experts (13% without rows) down 28.5 us weights-after against 30.1 us weights-first; 128
-  // tokens MXFP4 36.6 against 35.0 us.
+  // few experts lack rows (so_spec), else one K-step before the count and the rest after: an
+  // expert without rows then reads one step of its slice, not all of it (at three K-steps a
+  // unit's ring is its whole weight slice). Measured down pass: 32 tokens over 128 experts (13%
+  // without rows) 30.1 us all weights first, 28.6 us all after, 28.0 us one step first; 128
+  // tokens MXFP4 35.0 us all first against 36.6 us all after.
   const bool spec = !SO || p.so_spec;
   for (int m0 = 0;; m0 += 16) {
     Stage<WF, 1> buf[D];
     if (spec || m0 > 0) {
 #pragma unroll
       for (int s = 0; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
+    } else {
+      load_b<WF, 1, 1, AUX>(p, tr, 0, lane, buf[0]);  // one K-step before the count
     }
     // slot of each of the lane's four output rows (p.S: none)
     int rsid[4];
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, in
         }
         if (!spec) {
 #pragma unroll
-          for (int s = 0; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
+          for (int s = 1; s < D; ++s) load_b<WF, 1, 1, AUX>(p, tr, s, lane, buf[s]);
         }
       }
     }
