@@ -29,6 +29,7 @@ Tuning read_tuning() {
   t.prio = env_int("MXMOE_PRIO", -1);
   t.tile_pipe = env_int("MXMOE_TILE_PIPE", -1);
   t.slot_order = env_int("MXMOE_SLOT_ORDER", -1);
+  t.cap_units = env_int("MXMOE_CAP_UNITS", -1);
   t.final_nt = env_int("MXMOE_NT", -1);
   t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
   return t;

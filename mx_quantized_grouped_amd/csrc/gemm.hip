@@ -249,11 +249,12 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
   // (the grid is sized for the layout's capacity; ranges cut from the real tile count give every
   // XCD the same work, measured 57.9 -> 55.6 us for the 32-token gate_up); units run chunk-major,
   // tiles fastest, so the tiles of one expert on one chunk share an XCD.
-  const int nb = SO ? p.E + p.so_tiles : *p.num_post_pad / p.block_m;
+  const int nb = SO ? p.E + p.so_tiles : (p.cap_units ? n_blocks : *p.num_post_pad / p.block_m);
   const int total = n_chunks * nb;
   const int per_xcd = (total + 7) >> 3;
-  if (p.xcd_order && (int)(blockIdx.x >> 3) >= per_xcd) return;
-  const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
+  const bool ranges = p.xcd_order && !p.cap_units;
+  if (ranges && (int)(blockIdx.x >> 3) >= per_xcd) return;
+  const int u = ranges ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
   if (u >= total) return;
   const int chunk = u / nb, blk = u - chunk * nb;
   // slot order: rows r0 .. r1 - 1 of the unit are so_r[r] (slot ids)
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
   } else {
     r0 = blk * p.block_m;
     e = p.block_expert[blk];
+    if (e < 0) return;  // a tile past the layout's last (units over the capacity)
     r1 = r0 + p.block_m;
     tile_weights<WF, MT>(p, e, chunk * 4, tr);
   }
@@ -389,18 +391,20 @@ __host__ __device__ inline int sa_lds_bytes(int a_stride, int a_srs) {
 }
 
 template <int WF, int D, int AUX, bool SO = false>
-__global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, int n_groups) {
+__global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, int n_groups,
+                                                                 int n_blocks) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sa_lds[];
   constexpr bool A4 = a_is_fp4(WF);
   constexpr int SB = A4 ? KSTEP / 2 : KSTEP;  // code bytes of a row per K-step
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // unit (chunk group, tile), chunk-group-major, in contiguous per-XCD ranges (as k_gemm_stream)
-  const int nb = SO ? p.E + p.so_tiles : *p.num_post_pad / 16;
+  const int nb = SO ? p.E + p.so_tiles : (p.cap_units ? n_blocks : *p.num_post_pad / 16);
   const int total = n_groups * nb;
   const int per_xcd = (total + 7) >> 3;
-  if (p.xcd_order && (int)(blockIdx.x >> 3) >= per_xcd) return;
-  const int u = p.xcd_order ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
+  const bool ranges = p.xcd_order && !p.cap_units;
+  if (ranges && (int)(blockIdx.x >> 3) >= per_xcd) return;
+  const int u = ranges ? (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3) : (int)blockIdx.x;
   if (u >= total) return;  // uniform over the workgroup
   const int grp = u / nb, blk = u - grp * nb;
   const int chunk = grp * kSaWaves + wave;
@@ -424,6 +428,7 @@ __global__ __launch_bounds__(64 * kSaWaves) void k_gemm_down_sa(GemmParams p, in
     cnt = 16;
     hbase = 0;
     e = p.block_expert[blk];
+    if (e < 0) return;  // a tile past the layout's last (uniform over the workgroup)
   }
   TileRows<1> tr;
   tile_weights<WF, 1>(p, e, chunk * 4, tr);
@@ -986,10 +991,10 @@ hipError_t launch_down_sa(const GemmParams& p, int n_groups, int n_blocks, hipSt
   const size_t lds = (size_t)sa_lds_bytes(p.a_stride, p.a_srs);
   if (p.w_nt)
     hipLaunchKernelGGL((k_gemm_down_sa<WF, D, kNonTemporal, SO>), dim3(grid), dim3(64 * kSaWaves),
-                       lds, st, p, n_groups);
+                       lds, st, p, n_groups, n_blocks);
   else
     hipLaunchKernelGGL((k_gemm_down_sa<WF, D, 0, SO>), dim3(grid), dim3(64 * kSaWaves), lds, st,
-                       p, n_groups);
+                       p, n_groups, n_blocks);
   return hipGetLastError();
 }
 
@@ -1016,6 +1021,9 @@ hipError_t launch_slot_order(const GemmParams& p, int n_chunks, hipStream_t st) 
     default: return launch_stream<WF, GATE_UP, 1, 1, true>(p, n_chunks, ns, st);
   }
 }
+
+template <int WF, bool GATE_UP>
+hipError_t launch_small(const GemmParams& p0, int n_chunks, int n_blocks, hipStream_t st);
 
 template <int WF, bool GATE_UP>
 hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t st) {
@@ -1048,6 +1056,17 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
     return hipGetLastError();
   }
   if (p.so) return launch_slot_order<WF, GATE_UP>(p, n_chunks, st);
+  return launch_small<WF, GATE_UP>(p, n_chunks, n_blocks, st);
+}
+
+// Small-M launcher, sorted layout.
+template <int WF, bool GATE_UP>
+hipError_t launch_small(const GemmParams& p0, int n_chunks, int n_blocks, hipStream_t st) {
+  GemmParams p = p0;
+  // Few units (a handful of tokens: the capacity holds hardly more tiles than the layout uses):
+  // units over the capacity, so none waits for the tile count before its first weight loads.
+  if (tuning().cap_units != 0 && p.block_m == 16 && n_chunks * n_blocks <= kSplitKMaxUnits)
+    p.cap_units = 1;
   // Split K over 4 waves when the layout has fewer 16-row tiles than a quarter of the SIMDs' share
   // (a handful of tokens) and each wave keeps whole ring groups.
   if (WF != WF_BF16 && p.block_m == 16 && n_chunks * n_blocks <= kSplitKMaxUnits &&

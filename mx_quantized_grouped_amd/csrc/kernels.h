@@ -27,6 +27,7 @@ struct Tuning {
   int prio;            // MXMOE_PRIO: raised wave priority during the large-M MFMAs (0/1)
   int tile_pipe;       // MXMOE_TILE_PIPE: pipelined large-M K-steps (0/1)
   int slot_order;      // MXMOE_SLOT_ORDER: 0 = automatic plans never take the slot-order plan
+  int cap_units;       // MXMOE_CAP_UNITS: 0 = few-unit sorted plans decode units from the tile count
   int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
   int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
 };
@@ -139,6 +140,10 @@ struct GemmParams {
   // order over the grid; 0: one contiguous range per XCD)
   int xcd_run;
   int w_nt;  // small-M launcher: weight loads with the non-temporal hint
+  // small-M launcher, sorted layout with few units: units over the layout's capacity in plain
+  // order (a unit whose tile holds no expert, block_expert -1, ends at once), so no unit waits
+  // for the tile count before its first weight loads
+  int cap_units;
   // Slot-order plan (small-M launcher, no sort): so != 0. A unit is (column chunk, expert slot):
   // slots [0, E) are the routed experts, slots [E, E + so_tiles) the shared expert's tiles of 16
   // consecutive tokens. Every expert owns so_cap = T intermediate rows (expert-major, row
