@@ -32,6 +32,7 @@ Tuning read_tuning() {
   t.cap_units = env_int("MXMOE_CAP_UNITS", -1);
   t.final_nt = env_int("MXMOE_NT", -1);
   t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
+  t.down_rows = env_int("MXMOE_DOWN_ROWS", -1);
   return t;
 }
 }  // namespace
@@ -515,7 +516,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   g.xcd_order = tn.xcd_order >= 0 ? tn.xcd_order != 0 : 1;
   g.w_nt = tn.w_nt >= 0 ? tn.w_nt != 0 : 1;
   // large-M unit order: the options' run (-1: one contiguous range per XCD), else the A/B switch,
-  // else the default runs of 4 tiles
+  // else (-1 here) the launcher's own default
   auto unit_run = [&](int deflt, int env) { return P.unit_run ? (P.unit_run < 0 ? 0 : P.unit_run)
                                                               : (env >= 0 ? env : deflt); };
   if (e == hipSuccess) e = mark(1);
@@ -531,8 +532,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     gu.ws = (const uint8_t*)s13_p;
     gu.NT = 2 * P.I / 16;
     gu.NKS = P.H / KSTEP;
-    // large-M unit order: runs of 4 tiles (all their 256-column chunks) per XCD turn
-    gu.xcd_run = unit_run(P.I >= 128 ? 4 * (P.I / 128) : 1, tn.xcd_run_gu);
+    gu.xcd_run = unit_run(-1, tn.xcd_run_gu);
     e = launch_gate_up(P.wf, P.large, gu, n_blocks, st);
   }
   if (e == hipSuccess) e = mark(2);
@@ -546,7 +546,7 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
     dn.as_bytes = (uint32_t)((size_t)P.hrows * P.srs_I);
     dn.w = (const uint8_t*)w2_p;
     dn.ws = (const uint8_t*)s2_p;
-    dn.xcd_run = unit_run(P.H >= 256 ? 4 * (P.H / 256) : 1, tn.xcd_run_dn);
+    dn.xcd_run = unit_run(-1, tn.xcd_run_dn);
     dn.NT = P.H / 16;
     dn.NKS = P.Ip / KSTEP;
     if (P.fuse_final) {

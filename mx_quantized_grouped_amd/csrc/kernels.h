@@ -30,6 +30,7 @@ struct Tuning {
   int cap_units;       // MXMOE_CAP_UNITS: 0 = few-unit sorted plans decode units from the tile count
   int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
   int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
+  int down_rows;       // MXMOE_DOWN_ROWS: 0 = large-M down pass one chunk per workgroup
 };
 const Tuning& tuning();
 
@@ -137,7 +138,7 @@ struct GemmParams {
   // small-M launcher: 1 units in contiguous per-XCD ranges, 0 plain linear order over the grid
   int xcd_order;
   // large-M launcher: each XCD takes runs of xcd_run consecutive units in turn (1: plain linear
-  // order over the grid; 0: one contiguous range per XCD)
+  // order over the grid; 0: one contiguous range per XCD; -1: the launcher's default)
   int xcd_run;
   int w_nt;  // small-M launcher: weight loads with the non-temporal hint
   // small-M launcher, sorted layout with few units: units over the layout's capacity in plain
