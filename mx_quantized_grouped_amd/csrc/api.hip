@@ -33,6 +33,8 @@ Tuning read_tuning() {
   t.final_nt = env_int("MXMOE_NT", -1);
   t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
   t.down_rows = env_int("MXMOE_DOWN_ROWS", -1);
+  t.pf_steps = env_int("MXMOE_PF_STEPS", -1);
+  t.pf_wgs = env_int("MXMOE_PF_WGS", -1);
   return t;
 }
 }  // namespace
@@ -479,6 +481,27 @@ int mxmoe_forward_ex(const mxmoe_shape* s, const mxmoe_options* opt, const void*
   pa.zero_cnt = P.fuse_final ? done : nullptr;
   pa.n_cnt = P.fuse_final ? P.H / 64 : 0;
   pa.no_sort = P.so;
+  pa.pf_w = nullptr;
+  {
+    // slot-order gate_up: its units' first weight K-steps go into each XCD's L2 while the routing
+    // runs (the units' mapping onto XCDs is that of k_gemm_stream's per-XCD ranges)
+    const int pf_steps = tn.pf_steps >= 0 ? tn.pf_steps : kPrefetchSteps;
+    const int nks = P.H / KSTEP;
+    const bool ranges = tn.xcd_order != 0;
+    if (P.so && P.wf == WF_FP8 && ranges && pf_steps > 0 && pf_steps <= nks) {
+      const int fb = 2048;  // bytes of an fp8 weight fragment
+      pa.pf_w = (const uint8_t*)w13_p;
+      pa.pf_ws = (const uint8_t*)s13_p;
+      pa.pf_wbytes = (size_t)(2 * P.I / 16) * nks * fb;
+      pa.pf_sbytes = (size_t)(2 * P.I / 64) * nks * 256;
+      pa.pf_chunks = P.I / 32;
+      pa.pf_nb = P.E + P.so_tiles;
+      pa.pf_nks = nks;
+      pa.pf_step_bytes = 4 * fb;
+      pa.pf_steps = pf_steps;
+      pa.pf_wgs = tn.pf_wgs > 0 ? tn.pf_wgs : kPrefetchWgs;
+    }
+  }
   if (e == hipSuccess) e = launch_prologue(pa, s->logits_dtype == MXMOE_F32, aws, st);
   const int n_blocks = P.cap / P.bm;
   GemmParams g{};

@@ -20,6 +20,26 @@ enum WFmt { WF_FP8 = 0, WF_FP4 = 1, WF_BF16 = 2, WF_FP4A4 = 3 };
 __host__ __device__ constexpr bool w_is_fp4(int wf) { return wf == WF_FP4 || wf == WF_FP4A4; }
 __host__ __device__ constexpr bool a_is_fp4(int wf) { return wf == WF_FP4A4; }
 
+// ---------------------------------------------------------------------------- direct LDS loads
+// Raw buffer descriptor words (the raw-buffer format word of gfx9: loads past num_bytes return
+// zero) for the asm loads below.
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_bytes) {
+  const uint64_t a = (uint64_t)base;
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)num_bytes, 0x00020000};
+}
+
+// Direct global -> LDS loads: lane i's 16 (or 4) bytes land at LDS byte lds + 16 i (or 4 i).
+// They are issued from asm so that the compiler does not add its own (all-outstanding) waits
+// before every LDS read; the caller tracks completion with explicit s_waitcnt vmcnt.
+__device__ __forceinline__ void lds_load16(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+__device__ __forceinline__ void lds_load4(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
+}
+
 // ---------------------------------------------------------------------------- lane helpers
 __device__ __forceinline__ int lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));

@@ -568,23 +568,6 @@ constexpr int kLdsPitch = KSTEP;
 // Unit swizzle of an E2M1 activation row in LDS (r & 15 = the row within its 16-row group).
 __device__ __forceinline__ int a4_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// Raw buffer descriptor words (same format as raw_rsrc) for the asm loads below.
-__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t num_bytes) {
-  const uint64_t a = (uint64_t)base;
-  return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)num_bytes, 0x00020000};
-}
-
-// Direct global -> LDS loads: lane i's 16 (or 4) bytes land at LDS byte lds + 16 i (or 4 i).
-// They are issued from asm so that the compiler does not add its own (all-outstanding) waits
-// before every LDS read; completion is tracked explicitly with wait_loads_barrier.
-__device__ __forceinline__ void lds_load16(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
-}
-__device__ __forceinline__ void lds_load4(v4i rsrc, uint32_t lds, uint32_t voff, int soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               ::"s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "m0");
-}
 
 // Wait until at most N of this wave's vector-memory loads are outstanding and its LDS reads are
 // done, then barrier.

@@ -49,9 +49,46 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
   quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.a4, a.zero_out);
 }
 
-// Larger batches: workgroups [0, n_route) route 16 tokens each; the rest quantise / clear.
+// L2 prefetch (prefetch workgroup pb of the launch, on XCD blockIdx % 8 like every workgroup of a
+// launch): the first pf_steps K-steps of the weights and scales of each slot-order gate_up unit
+// that XCD will run, as direct LDS loads into a scratch area (nothing waits for them but the
+// workgroup's end). A unit's K-steps are contiguous in the prepacked layout.
+__device__ __forceinline__ void prefetch_gate_up(const PrologueArgs& a, int pb) {
+  __shared__ __attribute__((aligned(16))) uint8_t sink[(kThreads / 64) * 1024];
+  constexpr int kWaves = kThreads / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int x = blockIdx.x & 7, part = pb >> 3;
+  const int total = a.pf_chunks * a.pf_nb;
+  const int per_xcd = (total + 7) >> 3;
+  const int u0 = x * per_xcd, u1 = u0 + per_xcd < total ? u0 + per_xcd : total;
+  const int pieces = a.pf_steps * a.pf_step_bytes / 1024;  // 1 KiB weight loads per unit
+  const int per_unit = pieces + a.pf_steps;                // and a 256-byte scale load per step
+  const int nw = a.pf_wgs * kWaves;
+  const uint32_t lds =
+      (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)sink + 1024u * wave;
+  for (int i = part * kWaves + wave; i < (u1 - u0) * per_unit; i += nw) {
+    const int u = u0 + i / per_unit, q = i - (i / per_unit) * per_unit;
+    const int chunk = u / a.pf_nb, blk = u - chunk * a.pf_nb;
+    const int e = blk < a.E ? blk : a.E;
+    if (q < pieces) {
+      const v4i r = rsrc_words(a.pf_w + (size_t)e * a.pf_wbytes, (uint32_t)a.pf_wbytes);
+      lds_load16(r, lds, 16u * lane, chunk * a.pf_nks * a.pf_step_bytes + q * 1024);
+    } else {
+      const v4i r = rsrc_words(a.pf_ws + (size_t)e * a.pf_sbytes, (uint32_t)a.pf_sbytes);
+      lds_load4(r, lds, 4u * lane, (chunk * a.pf_nks + (q - pieces)) * 256);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Larger batches: workgroups [0, n_route) route 16 tokens each; the next n_quant quantise /
+// clear; any after them prefetch gate_up weights into L2.
 template <bool F32>
-__global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_route) {
+__global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_route, int n_quant) {
+  if ((int)blockIdx.x >= n_route + n_quant) {
+    prefetch_gate_up(a, (int)blockIdx.x - n_route - n_quant);
+    return;
+  }
   if ((int)blockIdx.x < n_route) {
     if (blockIdx.x == 0)
       for (int i = threadIdx.x; i < a.n_cnt; i += kThreads) a.zero_cnt[i] = 0;
@@ -64,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void k_route_quant(PrologueArgs a, int n_
   // grid-stride over the blocks (four lanes per block; a quad's lanes share every iteration)
   const int nbk = a.H / 32;
   const size_t nblk = (size_t)a.T * nbk;
-  const size_t nthr = (size_t)(gridDim.x - n_route) * kThreads;
+  const size_t nthr = (size_t)n_quant * kThreads;
   for (size_t g = (size_t)(blockIdx.x - n_route) * kThreads + threadIdx.x; (g >> 2) < nblk;
        g += nthr) {
     const size_t blk = g >> 2;
@@ -100,9 +137,11 @@ hipError_t launch_prologue(const PrologueArgs& a, bool logits_f32, void* align_s
     return hipGetLastError();
   }
   const int nr = (a.T + kThreads / 64 - 1) / (kThreads / 64);
-  dim3 grid(nr + (nq < kQuantMaxWgs ? nq : kQuantMaxWgs)), block(kThreads);
-  if (logits_f32) hipLaunchKernelGGL(k_route_quant<true>, grid, block, 0, st, a, nr);
-  else hipLaunchKernelGGL(k_route_quant<false>, grid, block, 0, st, a, nr);
+  const int nqw = nq < kQuantMaxWgs ? nq : kQuantMaxWgs;
+  const int npf = a.pf_w ? 8 * a.pf_wgs : 0;
+  dim3 grid(nr + nqw + npf), block(kThreads);
+  if (logits_f32) hipLaunchKernelGGL(k_route_quant<true>, grid, block, 0, st, a, nr, nqw);
+  else hipLaunchKernelGGL(k_route_quant<false>, grid, block, 0, st, a, nr, nqw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.no_sort) return e;
   return launch_align(a.ids, a.T, a.E, a.top_k, a.block_m, a.out, align_scratch, st);
