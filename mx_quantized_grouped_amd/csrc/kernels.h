@@ -31,7 +31,7 @@ struct Tuning {
   int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
   int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
   int down_rows;       // MXMOE_DOWN_ROWS: 0 = large-M down pass one chunk per workgroup
-  int pf_steps;        // MXMOE_PF_STEPS: K-steps of gate_up weights prefetched into L2 (0 off)
+  int pf_steps;        // MXMOE_PF_STEPS: K-steps of gate_up weights prefetched (0 off)
   int pf_wgs;          // MXMOE_PF_WGS: prefetch workgroups per XCD
 };
 const Tuning& tuning();
@@ -81,9 +81,11 @@ struct PrologueArgs {
   int32_t* zero_cnt;  // n_cnt counters to clear (null: none)
   int n_cnt;
   bool no_sort;     // slot-order plan: routing and quantisation only
-  // L2 prefetch of the slot-order gate_up weights (pf_w null: none): workgroups on each XCD load
-  // the first pf_steps K-steps of the units that XCD's gate_up workgroups will run (units over
-  // pf_chunks column chunks x pf_nb expert slots, contiguous per-XCD ranges), while the routing runs
+  // Prefetch of the slot-order gate_up weights (pf_w null: none): workgroups on each XCD load the
+  // first pf_steps K-steps of the units that XCD's gate_up workgroups will run (units over
+  // pf_chunks column chunks x pf_nb expert slots, contiguous per-XCD ranges), while the routing
+  // runs. gate_up's fetched bytes are unchanged by it (so not L2 hits); its gain comes from the
+  // memory-side cache or warm address translations.
   const uint8_t* pf_w;
   const uint8_t* pf_ws;
   size_t pf_wbytes, pf_sbytes;  // per expert: prepacked weight and scale bytes
@@ -168,7 +170,7 @@ struct GemmParams {
 };
 // Most tokens of a slot-order plan (rows of one expert, held in LDS by each unit).
 constexpr int kSlotOrderMaxT = 256;
-// L2 prefetch of the slot-order gate_up weights in the prologue (fp8 weights): K-steps per unit
+// Prefetch of the slot-order gate_up weights in the prologue (fp8 weights): K-steps per unit
 // and workgroups per XCD. Measured at 32 tokens, hidden 3072, 128 experts (block, two repeats):
 // off 82.7-83.1 us; 2 steps over 32 workgroups 81.6-82.3 (prologue +1.3, gate_up -3 us); 2, 4, 16,
 // 64 and 128 workgroups 126, 103, 85, 83-84 and 83-84 us (the prefetch workgroups' dispatch and

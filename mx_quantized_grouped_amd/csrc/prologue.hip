@@ -49,9 +49,9 @@ __global__ __launch_bounds__(kThreads) void k_prologue_small(PrologueArgs a) {
   quant_act_part(a.x, t, (int)(blk - t * nbk), (int)(g & 3), a.H, a.xq, a.xs, a.srs, a.a4, a.zero_out);
 }
 
-// L2 prefetch (prefetch workgroup pb of the launch, on XCD blockIdx % 8 like every workgroup of a
-// launch): the first pf_steps K-steps of the weights and scales of each slot-order gate_up unit
-// that XCD will run, as direct LDS loads into a scratch area (nothing waits for them but the
+// Weight prefetch (prefetch workgroup pb of the launch, on XCD blockIdx % 8 like every workgroup
+// of a launch): the first pf_steps K-steps of the weights and scales of each slot-order gate_up
+// unit that XCD will run, as direct LDS loads into a scratch area (nothing waits for them but the
 // workgroup's end). A unit's K-steps are contiguous in the prepacked layout.
 __device__ __forceinline__ void prefetch_gate_up(const PrologueArgs& a, int pb) {
   __shared__ __attribute__((aligned(16))) uint8_t sink[(kThreads / 64) * 1024];
