@@ -68,7 +68,21 @@ def _bf16_bits(v):
     return workloads.bf16_bits_from_f32(mx.round_to_bf16(v).astype(np.float32))
 
 
-@pytest.fixture(scope="module", params=CASES, ids=lambda c: "_".join(map(str, c)))
+def _applies(c, opt):
+    """The plans an option can take for a case: the one-launch path takes MX weights with E4M3
+    activations up to 128 tokens, the slot-order plan up to 256 tokens."""
+    T, fmt = c[0], c[5]
+    if opt == "one_launch":
+        return fmt not in ("bf16", "w4a4") and T <= 128
+    if opt == "slot_order":
+        return T <= 256
+    return True
+
+
+PAIRS = [(c, o) for c in CASES for o in OPTIONS if _applies(c, o)]
+
+
+@pytest.fixture(scope="module")
 def case(request):
     T, H, E, k, I, fmt = request.param
     _say("case", request.param)
@@ -123,16 +137,13 @@ def _ids(o):
     return "auto" if o is None else (o if isinstance(o, str) else "l%d_c%d_bm%d" % o)
 
 
-@pytest.mark.parametrize("opt", OPTIONS, ids=_ids)
+@pytest.mark.parametrize("case,opt", PAIRS, indirect=["case"],
+                         ids=["_".join(map(str, c)) + "-" + _ids(o) for c, o in PAIRS])
 def test_exact_output_and_intermediate(case, opt):
     c = case
     if opt == "one_launch":
-        if c["fmt"] in ("bf16", "w4a4") or c["T"] > 128:
-            pytest.skip("the one-launch path takes MX weights, E4M3 activations, up to 128 tokens")
         o = B.Options(0, 0, 0, 0, None, 1)
     elif opt == "slot_order":
-        if c["T"] > 256:
-            pytest.skip("the slot-order plan takes at most 256 tokens")
         o = B.Options(1, 1, 0, 0, None, 0, 0, 0, B.MXMOE_LAYOUT_SLOTS)
     else:
         o = None if opt is None else B.Options(opt[0], opt[1], opt[2], 0)
