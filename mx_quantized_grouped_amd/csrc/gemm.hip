@@ -18,6 +18,7 @@
 // more than one tile reads its weights from HBM once, the grouped-MoE program ordering of the
 // MiniMax-M3 page's local-shapes passage.
 #include <algorithm>
+#include <atomic>
 
 #include "device.h"
 #include "gemm_dev.h"
@@ -1181,13 +1182,21 @@ hipError_t launch_one(bool large, const GemmParams& p, int n_blocks, hipStream_t
       if (q.xcd_run <= 0) q.xcd_run = (total + 7) / 8;
       const int gq = 8 * q.xcd_run;
       const size_t lds = down_rows_lds_bytes(p.NKS);
-      static bool attr = false;  // the LDS limit above the 64 KiB default, set once
-      if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_down_rows<W>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)down_rows_lds_bytes(kDrMaxSteps));
+      // four K-steps of LDS stages exceed the 64 KiB default: raise the kernel's limit once per
+      // device (the attribute belongs to the current device's copy of the kernel)
+      if (lds > 65536) {
+        static std::atomic<uint64_t> attr_set{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
-        attr = true;
+        const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+        if (!bit || !(attr_set.load() & bit)) {
+          e = hipFuncSetAttribute((const void*)k_down_rows<W>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)down_rows_lds_bytes(kDrMaxSteps));
+          if (e != hipSuccess) return e;
+          attr_set.fetch_or(bit);
+        }
       }
       hipLaunchKernelGGL((k_down_rows<W>), dim3(((total + gq - 1) / gq) * gq), dim3(256), lds, st,
                          q, n_groups, n_blocks << sub_shift, sub_shift);

@@ -534,6 +534,7 @@ def test_forward_edge_shapes(T, H, E, k, I, fmt):
     (520, 384, 4, 2, 128, "mxfp8"),   # 3 K-steps: the step pairs end on a zero step
     (300, 128, 4, 3, 256, "mxfp4"),   # 1 K-step
     (700, 1024, 6, 2, 256, "mxfp8"),
+    (600, 1024, 4, 2, 512, "mxfp8"),  # row-resident down pass at 4 K-steps (70 KB of LDS stages)
 ])
 def test_forward_wide_tiles(T, H, E, k, I, fmt):
     _say("wide tiles", T, H, E, k, I, fmt)
