@@ -169,9 +169,14 @@ int mxmoe_route(const void* logits, int T, int E, int top_k, int logits_dtype,
  * returns 0). block_m in {16, 32, 64, 128, 256}. */
 size_t mxmoe_align_capacity(int T, int E, int top_k, int block_m);       /* host; 0 if invalid */
 size_t mxmoe_align_workspace_bytes(int T, int E, int top_k, int block_m); /* host */
+int mxmoe_align_ex(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
+                   int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                   int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream);
+/* The same sort without expert offsets or workspace: the library allocates nothing, so this form
+ * takes only sorts that need no scratch (those mxmoe_align_workspace_bytes sizes at 0: at most
+ * 4096 slots) and returns MXMOE_EWORKSPACE for larger ones (use mxmoe_align_ex). */
 int mxmoe_align(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
-                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
-                int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream);
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad, void* stream);
 
 /* ------------------------------------------------------------------------------ quantize
  * MX quantisation of a row-major matrix src [rows, K] (bf16 or fp32, finite) along K, one scale

@@ -28,7 +28,7 @@ FMT_BY_NAME = {"bf16": MXMOE_BF16, "f32": MXMOE_F32, "mxfp8": MXMOE_MXFP8_E4M3,
 
 EXPORTS = [
     "mxmoe_status_string", "mxmoe_gate", "mxmoe_gate_ex", "mxmoe_route", "mxmoe_align_capacity", "mxmoe_align_workspace_bytes",
-    "mxmoe_align", "mxmoe_quantize", "mxmoe_prepacked_bytes", "mxmoe_prepack",
+    "mxmoe_align", "mxmoe_align_ex", "mxmoe_quantize", "mxmoe_prepacked_bytes", "mxmoe_prepack",
     "mxmoe_workspace_bytes", "mxmoe_workspace_bytes_ex", "mxmoe_forward", "mxmoe_forward_ex",
     "mxmoe_workspace_view", "mxmoe_forward_noalloc",
 ]
@@ -93,7 +93,8 @@ def lib() -> ctypes.CDLL:
         "mxmoe_route": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
         "mxmoe_align_capacity": (sz, [i32, i32, i32, i32]),
         "mxmoe_align_workspace_bytes": (sz, [i32, i32, i32, i32]),
-        "mxmoe_align": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "mxmoe_align": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "mxmoe_align_ex": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
         "mxmoe_quantize": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
         "mxmoe_prepacked_bytes": (sz, [sp, i32]),
         "mxmoe_prepack": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -181,6 +182,8 @@ def mxmoe_align_workspace_bytes(T: int, E: int, top_k: int, block_m: int) -> int
 
 
 def mxmoe_align(topk_ids: torch.Tensor, E: int, block_m: int, with_expert_off=True, stream=None):
+    """The sort through mxmoe_align_ex (expert offsets, and the scratch a large sort needs, in
+    tensors allocated here)."""
     T, k1 = topk_ids.shape
     top_k = k1 - 1
     cap = mxmoe_align_capacity(T, E, top_k, block_m)
@@ -191,10 +194,13 @@ def mxmoe_align(topk_ids: torch.Tensor, E: int, block_m: int, with_expert_off=Tr
     eoff = torch.empty(E + 2, dtype=torch.int32, device=dev) if with_expert_off else None
     wsb = mxmoe_align_workspace_bytes(T, E, top_k, block_m)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    _check(lib().mxmoe_align(_ptr(topk_ids), T, E, top_k, block_m, _ptr(sorted_ids),
-                             _ptr(block_expert), _ptr(npp), _ptr(eoff), _ptr(ws), wsb,
-                             _stream(stream)), "mxmoe_align")
+    _check(lib().mxmoe_align_ex(_ptr(topk_ids), T, E, top_k, block_m, _ptr(sorted_ids),
+                                _ptr(block_expert), _ptr(npp), _ptr(eoff), _ptr(ws), wsb,
+                                _stream(stream)), "mxmoe_align_ex")
     return sorted_ids, block_expert, npp, eoff
+
+
+mxmoe_align_ex = mxmoe_align
 
 
 def mxmoe_quantize(src: torch.Tensor, fmt="mxfp8", codes=None, scales=None, stream=None):

@@ -299,8 +299,14 @@ size_t mxmoe_align_workspace_bytes(int T, int E, int top_k, int block_m) {
 }
 
 int mxmoe_align(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
-                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
-                int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream) {
+                int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad, void* stream) {
+  return mxmoe_align_ex(topk_ids, T, E, top_k, block_m, sorted_ids, block_expert, num_post_pad,
+                        nullptr, nullptr, 0, stream);
+}
+
+int mxmoe_align_ex(const int32_t* topk_ids, int T, int E, int top_k, int block_m,
+                   int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                   int32_t* expert_off, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_route_args(T, E, top_k);
   if (rc) return rc;
   if (!valid_block_m(block_m)) return MXMOE_EINVAL;

@@ -72,13 +72,24 @@ def test_align_validation_and_capacity(L):
     assert L.mxmoe_align_capacity(3, 2, 1, 2) == 0                       # block_m not allowed
     # S = 6 slots, at most min(E+1, S) = 3 touched experts: 6 + 3*15 = 51, rounded up to 16 -> 64
     assert L.mxmoe_align_capacity(3, 2, 1, 16) == 64
-    assert L.mxmoe_align(None, 3, 2, 1, 20, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
-    assert L.mxmoe_align(None, 0, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_OK
-    assert L.mxmoe_align(None, 3, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
+    assert L.mxmoe_align_ex(None, 3, 2, 1, 20, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
+    assert L.mxmoe_align_ex(None, 0, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_OK
+    assert L.mxmoe_align_ex(None, 3, 2, 1, 16, None, None, None, None, None, 0, None) == B.MXMOE_EINVAL
     # large variant needs scratch
     assert L.mxmoe_align_workspace_bytes(8192, 128, 8, 64) > 0
     p = ctypes.c_void_p(256)
-    assert L.mxmoe_align(p, 8192, 128, 8, 64, p, p, p, None, None, 0, None) == B.MXMOE_EWORKSPACE
+    assert L.mxmoe_align_ex(p, 8192, 128, 8, 64, p, p, p, None, None, 0, None) == B.MXMOE_EWORKSPACE
+
+
+def test_align_contract_form(L):
+    # the form without offsets or workspace: same validation; sorts that need scratch are refused
+    assert L.mxmoe_align(None, 3, 2, 1, 20, None, None, None, None) == B.MXMOE_EINVAL
+    assert L.mxmoe_align(None, 0, 2, 1, 16, None, None, None, None) == B.MXMOE_OK
+    assert L.mxmoe_align(None, 3, 2, 1, 16, None, None, None, None) == B.MXMOE_EINVAL
+    p = ctypes.c_void_p(256)
+    assert L.mxmoe_align_workspace_bytes(8192, 128, 8, 64) > 0
+    assert L.mxmoe_align(p, 8192, 128, 8, 64, p, p, p, None) == B.MXMOE_EWORKSPACE
+    assert L.mxmoe_align_workspace_bytes(455, 128, 8, 16) == 0   # 4095 slots: one workgroup
 
 
 def test_capacity_formula(L):

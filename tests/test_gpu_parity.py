@@ -235,6 +235,29 @@ def test_align_bit_exact(name, bm):
     assert np.array_equal(eoff.cpu().numpy(), L.expert_off)
 
 
+@pytest.mark.parametrize("name", ["decode_mxfp8", "wide512_mxfp4_T6"])
+def test_align_contract_form(name):
+    # mxmoe_align without offsets or workspace (sorts of at most 4096 slots), through the C ABI
+    import ctypes
+    _say("align contract form", name)
+    w, _, lb = inputs(name)
+    rid, _ = moe.route(f64(lb), w.top_k)
+    L = moe.align(rid, w.E, 16)
+    ids = torch.from_numpy(rid.astype(np.int32)).to(DEV)
+    cap = B.mxmoe_align_capacity(w.T, w.E, w.top_k, 16)
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=DEV)
+    bexp = torch.empty(cap // 16, dtype=torch.int32, device=DEV)
+    npp = torch.empty(1, dtype=torch.int32, device=DEV)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = B.lib().mxmoe_align(vp(ids), w.T, w.E, w.top_k, 16, vp(sorted_ids), vp(bexp), vp(npp),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert rc == B.MXMOE_OK
+    assert int(npp.item()) == L.num_post_pad
+    assert np.array_equal(sorted_ids.cpu().numpy(), L.sorted_ids)
+    assert np.array_equal(bexp.cpu().numpy(), L.block_expert)
+
+
 def test_align_random_shapes():
     _say("align random shapes")
     rng = np.random.default_rng(9)
