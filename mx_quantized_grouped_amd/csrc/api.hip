@@ -33,6 +33,7 @@ Tuning read_tuning() {
   t.final_nt = env_int("MXMOE_NT", -1);
   t.gate_tile = env_int("MXMOE_GATE_TILE", -1);
   t.down_rows = env_int("MXMOE_DOWN_ROWS", -1);
+  t.pair_fp4 = env_int("MXMOE_PAIR_FP4", -1);
   t.pf_steps = env_int("MXMOE_PF_STEPS", -1);
   t.pf_wgs = env_int("MXMOE_PF_WGS", -1);
   return t;

@@ -239,8 +239,25 @@ __device__ __forceinline__ void so_record(const GemmParams& p, int es, int nr, i
 // With a few hundred single-wave units (a handful of tokens) each wave's K stream is a chain of
 // memory round trips; split over KS waves the chain is KS times shorter.
 // SO: the slot-order plan (one wave per unit, one 16-row tile at a time).
-template <int WF, int MT, bool GATE_UP, int D, int KS, int AUX = 0, bool SO = false>
+// The MFMAs of one K-step with the activation fragments of stage sa_src and the weight fragments
+// of stage sb_src (the second chunk of a paired unit).
+template <int WF, int MT>
+__device__ __forceinline__ void mma_stage_b(const Stage<WF, MT>& sa_src, const Stage<WF, MT>& sb_src,
+                                            int ash, v4f (&acc)[MT][4]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    v8i a8;
+    a8.lo = sa_src.a[mt][0];
+    a8.hi = a_is_fp4(WF) ? v4i{0, 0, 0, 0} : sa_src.a[mt][1];
+    mma_frags<WF>(a8, (int)(sa_src.sa[mt] >> ash), sb_src.b, (int)sb_src.sb, acc[mt]);
+  }
+}
+
+// NG: 4-fragment weight groups per unit (2: a unit covers two adjacent column chunks with one
+// activation stream; slot-order gate_up with fp4 weights, where a chunk's K-step is 4 KB).
+template <int WF, int MT, bool GATE_UP, int D, int KS, int AUX = 0, bool SO = false, int NG = 1>
 __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chunks, int n_blocks) {
+  static_assert(NG == 1 || (GATE_UP && SO), "paired chunks: slot-order gate_up only");
   static_assert(GATE_UP || MT == 1, "the down epilogue of this launcher handles one 16-row tile");
   static_assert(KS == 1 || MT == 1, "split K reduces one 16-row tile");
   static_assert(!SO || (KS == 1 && MT == 1), "slot order: one wave, one 16-row tile");
@@ -266,13 +283,20 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
   // the loads of group k0 + D while multiplying group k0 without any branch, and the last group
   // is peeled. Weight loads of the first group go out before the (dependent) row lookup.
   Stage<WF, MT> buf[D];
+  Stage<WF, MT> bufB[NG == 2 ? D : 1];  // second chunk's weights (its activation part is unused)
+  TileRows<MT> trB;
   if constexpr (SO) {
     // the unit's expert is known: its first weight K-steps go out before the scan for its rows
     // (an expert without rows then drops D K-steps of one chunk)
     e = blk < p.E ? blk : p.E;
-    tile_weights<WF, MT>(p, e, chunk * 4, tr);
+    tile_weights<WF, MT>(p, e, chunk * 4 * NG, tr);
+    trB = tr;
+    trB.nt0 = tr.nt0 + 4;
 #pragma unroll
-    for (int s = 0; s < D; ++s) load_b<WF, MT, MT, AUX>(p, tr, s, lane, buf[s]);
+    for (int s = 0; s < D; ++s) {
+      load_b<WF, MT, MT, AUX>(p, tr, s, lane, buf[s]);
+      if constexpr (NG == 2) load_b<WF, MT, MT, AUX>(p, trB, s, lane, bufB[s]);
+    }
     r0 = 0;
     r1 = so_rows(p, blk, lane, so_r);
     if (GATE_UP && chunk == 0) so_record(p, blk, r1, lane, so_r);
@@ -295,15 +319,24 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
   // slot order: intermediate row of unit row r (the expert's rows, then the shared tile's offset)
   const int hbase = SO ? e * p.so_cap + (blk < p.E ? 0 : 16 * (blk - p.E)) : 0;
   for (int m0 = r0; m0 < r1; m0 += 16 * MT) {
-    v4f acc[MT][4];
+    v4f acc[MT][4], accB[NG == 2 ? MT : 1][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int f = 0; f < 4; ++f) acc[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NG == 2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) accB[mt][f] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
     const int nk = p.NKS / KS;  // K-steps of this wave: global step wave + KS * i
     if (!SO || m0 != r0) {  // slot order: the first tile's ring went out before the scan
 #pragma unroll
-      for (int s = 0; s < D; ++s) load_b<WF, MT, MT, AUX>(p, tr, wave + KS * s, lane, buf[s]);
+      for (int s = 0; s < D; ++s) {
+        load_b<WF, MT, MT, AUX>(p, tr, wave + KS * s, lane, buf[s]);
+        if constexpr (NG == 2) load_b<WF, MT, MT, AUX>(p, trB, wave + KS * s, lane, bufB[s]);
+      }
     }
     // down: slot id and routing weight of the lane's four output rows, fetched now so the
     // epilogue does not wait for them
@@ -332,11 +365,18 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         mma_stage<WF, MT>(buf[s], 8 * g, acc);
+        if constexpr (NG == 2) {
+          mma_stage_b<WF, MT>(buf[s], bufB[s], 8 * g, accB);
+          load_b<WF, MT, MT, AUX>(p, trB, wave + KS * (k0 + s + D), lane, bufB[s]);
+        }
         load_stage<WF, MT, AUX>(p, tr, wave + KS * (k0 + s + D), lane, buf[s]);
       }
     }
 #pragma unroll
-    for (int s = 0; s < D; ++s) mma_stage<WF, MT>(buf[s], 8 * g, acc);
+    for (int s = 0; s < D; ++s) {
+      mma_stage<WF, MT>(buf[s], 8 * g, acc);
+      if constexpr (NG == 2) mma_stage_b<WF, MT>(buf[s], bufB[s], 8 * g, accB);
+    }
     if constexpr (KS > 1) {
       __shared__ v4f part[KS][4][64];
 #pragma unroll
@@ -365,7 +405,8 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_stream(GemmParams p, int n_chu
       } else {
         layout_rows<MT>(m0, r1, g, hrow);
       }
-      epilogue_gate_up<WF, MT>(p, acc, hrow, chunk, n);
+      epilogue_gate_up<WF, MT>(p, acc, hrow, chunk * NG, n);
+      if constexpr (NG == 2) epilogue_gate_up<WF, MT>(p, accB, hrow, chunk * 2 + 1, n);
     } else {
       epilogue_down_rows(p, acc[0], rsid, rw, chunk, n);
     }
@@ -1106,15 +1147,15 @@ inline bool tile_pipe(bool gate_up, int wf) {
 }
 
 // n_blocks: the layout's tile capacity, or the expert slots of the slot-order plan
-template <int WF, bool GATE_UP, int D, int KS = 1, bool SO = false>
+template <int WF, bool GATE_UP, int D, int KS = 1, bool SO = false, int NG = 1>
 hipError_t launch_stream(const GemmParams& p, int n_chunks, int n_blocks, hipStream_t st) {
   const int total = n_chunks * n_blocks;
   const int grid = ((total + 7) / 8) * 8;
   if (p.w_nt)
-    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, kNonTemporal, SO>), dim3(grid),
+    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, kNonTemporal, SO, NG>), dim3(grid),
                        dim3(64 * KS), 0, st, p, n_chunks, n_blocks);
   else
-    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, 0, SO>), dim3(grid), dim3(64 * KS),
+    hipLaunchKernelGGL((k_gemm_stream<WF, 1, GATE_UP, D, KS, 0, SO, NG>), dim3(grid), dim3(64 * KS),
                        0, st, p, n_chunks, n_blocks);
   return hipGetLastError();
 }
@@ -1148,6 +1189,15 @@ hipError_t launch_slot_order(const GemmParams& p, int n_chunks, hipStream_t st) 
         default: return launch_down_sa<WF, 1, true>(p, n_chunks / kSaWaves, ns, st);
       }
     }
+  }
+  if constexpr (GATE_UP && w_is_fp4(WF)) {
+    // fp4 weights: a unit takes two adjacent chunks (one activation stream, 8 KB of weights per
+    // K-step as with fp8) with a 3-deep ring where the K-step count allows
+    const int pd = tuning().pair_fp4 < 0 ? 3 : tuning().pair_fp4;  // ring depth, 0: off
+    if (n_chunks % 2 == 0 && pd == 4 && p.NKS % 4 == 0)
+      return launch_stream<WF, GATE_UP, 4, 1, true, 2>(p, n_chunks / 2, ns, st);
+    if (n_chunks % 2 == 0 && pd == 3 && p.NKS % 3 == 0)
+      return launch_stream<WF, GATE_UP, 3, 1, true, 2>(p, n_chunks / 2, ns, st);
   }
   switch (d) {
     case 4: return launch_stream<WF, GATE_UP, (WF == WF_BF16 ? 1 : 4), 1, true>(p, n_chunks, ns, st);

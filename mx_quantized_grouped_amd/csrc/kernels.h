@@ -31,6 +31,7 @@ struct Tuning {
   int final_nt;        // MXMOE_NT: non-temporal slot-row loads of the final sum (0/1)
   int gate_tile;       // MXMOE_GATE_TILE: router gate tile (10 TM + F, +100 LDS-staged)
   int down_rows;       // MXMOE_DOWN_ROWS: 0 = large-M down pass one chunk per workgroup
+  int pair_fp4;        // MXMOE_PAIR_FP4: ring depth (3, 4) of paired fp4 gate_up units, 0 off
   int pf_steps;        // MXMOE_PF_STEPS: K-steps of gate_up weights prefetched (0 off)
   int pf_wgs;          // MXMOE_PF_WGS: prefetch workgroups per XCD
 };
