@@ -196,7 +196,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("src", help="directory with the prof_trace_* / prof_pmc_* run outputs")
     ap.add_argument("--traffic", nargs="*", default=[
-        "decode_mxfp8=k_gemm_stream<0, 1, true, 3, 1, 2, true>",
+        "decode_mxfp8=k_gemm_stream<0, 1, true, 3, 1, 2, true, 1>",
         "prefill_mxfp8=k_gemm_tile<0, true, true, true>"],
         help="WORKLOAD=gate_up kernel name, for the counter summary")
     ap.add_argument("--mfma", nargs="*", default=[],
