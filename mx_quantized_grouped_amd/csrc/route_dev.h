@@ -92,14 +92,15 @@ __device__ void route_select(uint32_t (&vkey)[NPER], int t, int E, int top_k, in
     const uint32_t bv = wave_max_u32(lbest);
     uint32_t be;
     if (F32) {
-      // among the experts holding the best value, the lowest index
-      uint32_t lidx = 0;
+      // among the experts holding the best value, the lowest index: expert lane + 64 c, so the
+      // lowest column with a match and its lowest lane, from one ballot per column (scalar bit
+      // scans instead of a second wave reduction)
+      be = 0;
 #pragma unroll
-      for (int c = 0; c < NPER; ++c) {
-        uint32_t ci = 0xFFFFu - (uint32_t)(lane + 64 * c);
-        if (vkey[c] == bv && ci > lidx) lidx = ci;
+      for (int c = NPER - 1; c >= 0; --c) {
+        const uint64_t m = __ballot(vkey[c] == bv);
+        if (m) be = 64u * (uint32_t)c + (uint32_t)__builtin_ctzll(m);
       }
-      be = 0xFFFFu - wave_max_u32(lidx);
     } else {
       be = 0xFFFFu - (bv & 0xFFFFu);
     }
