@@ -1162,6 +1162,9 @@ hipError_t launch_stream(const GemmParams& p, int n_chunks, int n_blocks, hipStr
 
 template <int WF, int D, bool SO = false>
 hipError_t launch_down_sa(const GemmParams& p, int n_groups, int n_blocks, hipStream_t st) {
+  // the ring's steady loop and its peeled last group assume D divides the K-step count; another
+  // depth would run a step past the end of the tile's rows
+  if (p.NKS % D != 0) return hipErrorInvalidValue;
   const int total = n_groups * n_blocks;
   const int grid = ((total + 7) / 8) * 8;
   const size_t lds = (size_t)sa_lds_bytes(p.a_stride, p.a_srs);
